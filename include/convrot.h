@@ -1,0 +1,190 @@
+/*
+ * convrot.h -- C ABI of the MI355X (gfx950) W8A8 ConvRot expert-choice MoE library (libconvrot_amd.so).
+ *
+ * What is computed (pages cited by title and section):
+ *  - "Nucleus-Image INT8 Convrot Experts + FP8 Text Encoder" model card, "Quantization": each routed-expert
+ *    matrix is rotated with ConvRot (a block Hadamard rotation along the input dimension; group 256 for the
+ *    gate/up projection, 64 for the down projection), quantised to symmetric INT8 with nearest rounding and
+ *    one FP32 scale per output row, and run through W8A8 ConvRot linears with BF16 outputs.
+ *  - "NitroFusion2 for ComfyUI: int8, W6A8, W4A8", "How they were made": the int8 format is that block
+ *    Hadamard rotation, one scale per row and 8-bit activations; rotation and rounding happen in fp32.
+ *  - "MLX Nucleus-Image", overview and "Conversion notes": 64 routed experts with expert-choice routing (each
+ *    expert picks its top-C tokens and the outputs are scattered back to the tokens); the expert SwiGLU is
+ *    silu(gate) * up with the first half of the fused projection the gate.
+ *  - "XB_UNetLoaderINTROCm", "The mechanism, briefly": multiply in INT8, dequantise on the fly.
+ *
+ * Numerics (identical on every entry point):
+ *  - Rotation: per contiguous block of g values along K, v -> v . H_g / sqrt(g) with H_g the Sylvester
+ *    Hadamard matrix in natural order, evaluated in fp32 as the fast transform with stages h = 1, 2, ..., g/2
+ *    (pair (j, j+h) -> (a + b, a - b)) and then the exact power-of-two scale.  g is 64 or 256.
+ *  - Quantiser, per row over all K: scale = max|r| / qmax (fp32 division), code = clamp(rint(r / scale),
+ *    -qmax, qmax) (fp32 division, ties to even); scale 0 gives codes 0.  qmax = 127 (INT8) or 7 (INT4).
+ *    Activations get one scale per token (row) computed from the call's own data.
+ *  - Product: exact INT32 sum of INT8 x INT8 (|acc| <= K * 127^2, so K <= 133144).
+ *  - Dequantisation: bf16_rne( ((float)acc * s_act) * s_w ) [+ (float)bias, added before the rounding].
+ *  - SwiGLU: a = bf16_rne( silu(g) * u ), silu(g) = g / (1 + E(-g)), g and u the bf16 gate/up outputs.
+ *  - Router: p[t, :] = softmax over experts in fp32 (max-subtracted, E() of the differences, sum in ascending
+ *    expert order, one division per entry).  Expert e takes the C tokens with the largest p[:, e], ties to the
+ *    lower token index, listed in ascending token order; its gate weight is that p (not renormalised).
+ *  - Combine: out[t, :] = bf16_rne( sum over experts e in ascending order that took t of w * (float)z ),
+ *    fp32, starting from +0.0f; a token taken by no expert gets +0.
+ *  - E(x) is a fixed fp32 exponential: n = rint(x * log2e), r = (x - n*ln2_hi) - n*ln2_lo with ln2_hi = ln 2
+ *    rounded to 16 significant bits (Cody-Waite reduction), Taylor series of e^r through r^7 in Horner form
+ *    (coefficients 1/k! rounded to fp32), scaled by 2^n; E(x) = 0 for x < -86 and +inf for x > 88.  Every
+ *    fp32 step above is a separate IEEE operation (no fused multiply-add), so results are reproducible
+ *    bit for bit.
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) are device memory on the current HIP device; bf16 crosses the ABI as raw
+ *    uint16_t bits.  The caller owns every buffer; the library allocates nothing and keeps no state between
+ *    calls, so calls are thread-safe.  Calls only enqueue work on `stream` (0 = the null stream) and return.
+ *  - Arguments are validated on the host before anything is enqueued; on an error nothing is written.
+ *    CONVROT_ERR_HIP means a launch failed after validation; outputs are then unspecified.
+ *  - Row strides equal the row length (dense row-major).  Every device pointer must be 16-byte aligned.
+ *  - NaN or Inf in activations or logits are outside the contract (no per-call scan); the weight converter
+ *    rejects non-finite weights with CONVROT_ERR_NONFINITE.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum convrot_status {
+    CONVROT_OK = 0,
+    CONVROT_ERR_NULL = 1,       /* a required pointer is NULL */
+    CONVROT_ERR_SHAPE = 2,      /* a size is out of range or inconsistent */
+    CONVROT_ERR_GROUP = 3,      /* rotation group not 64/256, or the dimension is not a multiple of it */
+    CONVROT_ERR_BITS = 4,       /* weight bits not 8 or 4 */
+    CONVROT_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
+    CONVROT_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than the matching *_workspace_bytes() */
+    CONVROT_ERR_NONFINITE = 7,  /* the weight converter found NaN or Inf */
+    CONVROT_ERR_HIP = 8         /* a HIP launch or runtime call failed */
+} convrot_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* convrot_status_str(convrot_status s);
+
+/* Quantised weights of one routed-expert MoE layer.  The struct itself lives in host memory. */
+typedef struct convrot_moe_weights {
+    int E;             /* routed experts, >= 1 */
+    int d;             /* model width (gate/up input, down output), multiple of group_gu */
+    int I;             /* expert hidden width (down input), multiple of group_dn and of 64 */
+    int group_gu;      /* rotation group of gate/up: 64 or 256 (the pages use 256) */
+    int group_dn;      /* rotation group of down: 64 or 256 (the pages use 64) */
+    int wbits;         /* 8: int8 codes; 4: nibble-packed int4 codes (even k in bits 0-3) */
+    const void* q_gu;  /* (device) [E, 2I, d] int8, or [E, 2I, d/2] u8; rows 0..I-1 gate, I..2I-1 up */
+    const float* s_gu; /* (device) [E, 2I] fp32 per-output-row scales */
+    const void* q_dn;  /* (device) [E, d, I] int8, or [E, d, I/2] u8 */
+    const float* s_dn; /* (device) [E, d] fp32 */
+} convrot_moe_weights;
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Offline weight converter  (model card "Quantization": rotate each expert matrix, quantise per row)     */
+/* ---------------------------------------------------------------------------------------------------- */
+
+/* w (device) [E, N, K] bf16 -> q_out (device) int8 [E, N, K] (bits = 8) or u8 [E, N, K/2] (bits = 4), and
+ * scale_out (device) [E, N] fp32.  Each row is rotated along K in blocks of `group` and quantised with its
+ * own scale (qmax 127 or 7).  Requires E, N >= 1, 1 <= K <= 8192, K % group == 0.  A non-finite weight
+ * makes the call return CONVROT_ERR_NONFINITE after the stream work completes (this call synchronises
+ * `stream`); outputs are then unspecified. */
+convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits,
+                                        void* q_out, float* scale_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Single W8A8 ConvRot linear  (model card "Quantization": W8A8 ConvRot linear with BF16 outputs)          */
+/* ---------------------------------------------------------------------------------------------------- */
+
+/* Bytes of workspace convrot_linear_w8a8 needs for an [M, K] input. */
+size_t convrot_linear_workspace_bytes(int M, int K);
+
+/* y[M, N] = bf16( ((float)(rotq(x) . qw^T) * sx) * sw ) (+ bias).  x (device) [M, K] bf16; qw (device)
+ * [N, K] int8 from convrot_quantize_weights with the same group; sw (device) [N]; bias (device) [N] bf16
+ * or NULL; y (device) [M, N] bf16; ws (device) at least convrot_linear_workspace_bytes(M, K).
+ * Requires M, N >= 1, K <= 8192, K % group == 0, group 64 or 256. */
+convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t* qw, const float* sw, int N,
+                                   int group, const uint16_t* bias, uint16_t* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Expert-choice MoE layer, routed experts  ("MLX Nucleus-Image": expert-choice, silu(gate) * up)          */
+/* ---------------------------------------------------------------------------------------------------- */
+
+/* Bytes of workspace moe_expert_choice_forward needs. */
+size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights* w);
+
+/* x (device) [T, d] bf16; router_logits (device) [T, E] fp32; out (device) [T, d] bf16, overwritten;
+ * idx_out (device) [E, C] int32 or NULL; wt_out (device) [E, C] fp32 or NULL (the routing decisions);
+ * ws (device) at least moe_expert_choice_workspace_bytes(T, C, w).
+ * Steps: softmax + top-C per expert; rotate+quantise x (group_gu); grouped INT8 gate/up GEMM over each
+ * expert's C gathered tokens with fused dequant + SwiGLU; rotate+quantise the hidden rows (group_dn);
+ * grouped INT8 down GEMM with dequant; probability-weighted combine into out.
+ * Requires 1 <= C <= T, E >= 1, d % group_gu == 0, I % group_dn == 0, I % 64 == 0, d and I <= 8192. */
+convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* router_logits, int C,
+                                         const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                         float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Stage entry points: each step of the forward on its own, so that every stage can be checked exactly     */
+/* given identical inputs.  Same kernels as the forward.                                                   */
+/* ---------------------------------------------------------------------------------------------------- */
+
+/* Rotate + quantise rows (activations: qmax 127, one scale per row).  x (device) [rows, K] bf16 ->
+ * q_out (device) [rows, K] int8, s_out (device) [rows] fp32, rot_out (device) [rows, K] fp32 rotated
+ * values before quantisation, or NULL.  Requires rows >= 0, 1 <= K <= 8192, K % group == 0; rows == 0 is a
+ * no-op (pointers may then be NULL). */
+convrot_status convrot_rotq_rows(const uint16_t* x, int64_t rows, int K, int group, int8_t* q_out, float* s_out,
+                                 float* rot_out, hipStream_t stream);
+
+/* Quantise already-rotated fp32 rows: r (device) [rows, K] -> q_out (device) [rows, K] int8 codes (bits 8:
+ * qmax 127; bits 4: qmax 7, unpacked) and s_out (device) [rows].  Requires K % 8 == 0, K <= 8192; rows == 0
+ * is a no-op. */
+convrot_status convrot_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q_out,
+                                           float* s_out, hipStream_t stream);
+
+/* acc_out[M, N] = a[M, K] . b[N, K]^T exactly in int32, with the same INT8 MFMA main loop as the layer.
+ * Requires M, N >= 1, 16 <= K <= 133144, K % 16 == 0. */
+convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int N, int K, int32_t* acc_out,
+                                   hipStream_t stream);
+
+/* Bytes of workspace moe_route_expert_choice needs. */
+size_t moe_route_workspace_bytes(int T, int E);
+
+/* Router alone.  in (device) [T, E]: logits (is_probs = 0) or probabilities (is_probs = 1, used as given);
+ * idx_out (device) [E, C] int32; wt_out (device) [E, C] fp32; probs_out (device) [T, E] or NULL.
+ * Requires 1 <= C <= T, E >= 1. */
+convrot_status moe_route_expert_choice(const float* in, int is_probs, int T, int E, int C, int32_t* idx_out,
+                                       float* wt_out, float* probs_out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* Gate/up stage: for every expert e and slot c, token t = idx[e, c]:
+ * a_out[e*C + c, :] = SwiGLU of the dequantised gate/up product of qx[t] (device [T, d] int8, scale
+ * sx[t], device [T] fp32) with expert e.  idx (device) [E, C] with entries in [0, T); a_out (device)
+ * [E*C, I] bf16. */
+convrot_status moe_gateup_swiglu(const int8_t* qx, const float* sx, int T, const int32_t* idx, int C,
+                                 const convrot_moe_weights* w, uint16_t* a_out, hipStream_t stream);
+
+/* Down stage: z_out[e*C + c, :] = bf16(dequant(qa[e*C + c] . q_dn[e]^T)).  qa (device) [E*C, I] int8,
+ * sa (device) [E*C] fp32, z_out (device) [E*C, d] bf16. */
+convrot_status moe_down_proj(const int8_t* qa, const float* sa, int C, const convrot_moe_weights* w,
+                             uint16_t* z_out, hipStream_t stream);
+
+/* Bytes of workspace moe_combine needs. */
+size_t moe_combine_workspace_bytes(int T, int E);
+
+/* Combine stage: out[T, d] from z (device) [E*C, d] bf16, idx (device) [E, C] (each row strictly
+ * ascending, entries in [0, T)) and wt (device) [E, C]. */
+convrot_status moe_combine(const uint16_t* z, const int32_t* idx, const float* wt, int T, int E, int C, int d,
+                           uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -15,7 +15,7 @@ __all__ = [
     "build", "load", "bf16_round", "bf16_to_f32", "exp", "silu", "rotate_rows_f32", "rotate_rows_bf16",
     "quantize_rows", "rotq_rows", "pack_int4", "unpack_int4", "quantize_weights", "gemm_i8_i32",
     "dequant_bf16", "linear_w8a8", "softmax_experts", "route_from_probs", "route", "swiglu", "combine",
-    "moe_gateup", "moe_down", "moe_forward",
+    "moe_gateup", "moe_down", "moe_forward", "moe_rows",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,7 @@ def _declare(lib):
         "oracle_moe_down": (None, [_p, _p, _i, _i, _i, _i, _p, _p, _i, _p]),
         "oracle_moe_forward": (_i, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _i,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+        "oracle_moe_rows": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _p, _p, _p, _p, _i, _i, _p, _i, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -340,3 +341,24 @@ def moe_forward(x, logits, C: int, q_gu, s_gu, g_gu: int, q_dn, s_dn, g_dn: int,
         _ptr(r["out"]), _ptr(r["idx"]), _ptr(r["wt"]), _ptr(g("p")), _ptr(g("qx")), _ptr(g("sx")), _ptr(g("a")),
         _ptr(g("qa")), _ptr(g("sa")), _ptr(g("z"))), "moe_forward")
     return r
+
+
+def moe_rows(qx, sx, idx, wt, q_gu, s_gu, q_dn, s_dn, g_dn: int, tokens, wbits: int = 8) -> np.ndarray:
+    """Layer output rows (bf16 bits [len(tokens), d]) for the given tokens only."""
+    qx = _c(qx, np.int8)
+    sx = _c(sx, np.float32)
+    idx = _c(idx, np.int32)
+    wt = _c(wt, np.float32)
+    q_gu = np.ascontiguousarray(q_gu)
+    q_dn = np.ascontiguousarray(q_dn)
+    s_gu = _c(s_gu, np.float32)
+    s_dn = _c(s_dn, np.float32)
+    tokens = _c(tokens, np.int32)
+    E, C = idx.shape
+    d = qx.shape[1]
+    I = s_gu.shape[1] // 2
+    out = np.empty((tokens.size, d), np.uint16)
+    _check(load().oracle_moe_rows(_ptr(qx), _ptr(sx), d, _ptr(idx), _ptr(wt), E, C, I, _ptr(q_gu), _ptr(s_gu),
+                                  _ptr(q_dn), _ptr(s_dn), g_dn, wbits, _ptr(tokens), tokens.size, _ptr(out)),
+           "moe_rows")
+    return out

@@ -171,6 +171,7 @@ int oracle_rotate_rows_bf16(const uint16_t* in, int64_t rows, int K, int g, floa
     int k4 = log4_of(g);
     if (k4 < 0 || K % g) return -1;
     float norm = ldexpf(1.0f, -k4);
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         float* o = out + r * (int64_t)K;
         for (int k = 0; k < K; ++k) o[k] = bf16_to_f32(in[r * (int64_t)K + k]);
@@ -184,6 +185,7 @@ int oracle_rotate_rows_bf16(const uint16_t* in, int64_t rows, int K, int g, floa
 /* ------------------------------------------------------------------------------------------------- */
 
 void oracle_quantize_rows(const float* r, int64_t rows, int K, int qmax, int8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
         const float* v = r + i * (int64_t)K;
         float amax = 0.0f;
@@ -525,4 +527,63 @@ int oracle_moe_forward(const uint16_t* x, int T, int d, const float* logits, int
     free(sa);
     free(z);
     return st;
+}
+
+/* Layer output rows for a list of tokens only, for checking large layers at sampled tokens.  Given the
+ * routing (idx, wt) and the quantised tokens (qx, sx), out_rows[i, :] is the output of token tokens[i]:
+ * the same per-(expert, slot) arithmetic as oracle_moe_forward (gate/up, SwiGLU, rotate + quantise with
+ * group g_dn, down) and the same combine order (experts ascending). */
+int oracle_moe_rows(const int8_t* qx, const float* sx, int d, const int32_t* idx, const float* wt, int E, int C,
+                    int I, const void* q_gu, const float* s_gu, const void* q_dn, const float* s_dn, int g_dn,
+                    int wbits, const int32_t* tokens, int ntok, uint16_t* out_rows) {
+    if (log4_of(g_dn) < 0 || I % g_dn || (wbits != 8 && wbits != 4)) return -1;
+    int8_t* wg = expert_codes(q_gu, wbits, (int64_t)E * 2 * I, d);
+    int8_t* wd = expert_codes(q_dn, wbits, (int64_t)E * d, I);
+    if (!wg || !wd) {
+        free(wg);
+        free(wd);
+        return -2;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < ntok; ++i) {
+        int t = tokens[i];
+        float* acc = (float*)malloc(sizeof(float) * (size_t)d);
+        uint16_t* gu = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)I);
+        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+        int8_t* qa = (int8_t*)malloc((size_t)I);
+        for (int j = 0; j < d; ++j) acc[j] = 0.0f;
+        for (int e = 0; e < E; ++e) {
+            int c = -1;
+            for (int k = 0; k < C; ++k)
+                if (idx[(int64_t)e * C + k] == t) c = k;
+            if (c < 0) continue;
+            const int8_t* xr = qx + (int64_t)t * d;
+            for (int n = 0; n < 2 * I; ++n) {
+                const int8_t* wr = wg + ((int64_t)e * 2 * I + n) * d;
+                int32_t s = 0;
+                for (int k = 0; k < d; ++k) s += (int32_t)xr[k] * (int32_t)wr[k];
+                gu[n] = f32_to_bf16(dequant(s, sx[t], s_gu[(int64_t)e * 2 * I + n]));
+            }
+            oracle_swiglu(gu, 1, I, a);
+            float sa;
+            oracle_rotq_rows(a, 1, I, g_dn, 127, qa, &sa, NULL);
+            float w = wt[(int64_t)e * C + c];
+            for (int n = 0; n < d; ++n) {
+                const int8_t* wr = wd + ((int64_t)e * d + n) * I;
+                int32_t s = 0;
+                for (int k = 0; k < I; ++k) s += (int32_t)qa[k] * (int32_t)wr[k];
+                float z = bf16_to_f32(f32_to_bf16(dequant(s, sa, s_dn[(int64_t)e * d + n])));
+                float prod = w * z;
+                acc[n] = acc[n] + prod;
+            }
+        }
+        oracle_bf16_round(acc, d, out_rows + (int64_t)i * d);
+        free(acc);
+        free(gu);
+        free(a);
+        free(qa);
+    }
+    free(wg);
+    free(wd);
+    return 0;
 }

@@ -1,0 +1,97 @@
+"""The C ABI on the host, no GPU needed: the library loads, exports every function include/convrot.h declares,
+and rejects invalid arguments (validation runs before anything touches the GPU)."""
+import ctypes
+
+import pytest
+
+from w8a8_rotated_int8_amd import binding as cr
+
+OK, NULL, SHAPE, GROUP, BITS, ALIGN, WS = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000  # a 16-byte aligned stand-in pointer: never dereferenced, validation rejects first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return cr.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = cr.header_functions()
+    assert len(names) == 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(cr._SIGS)
+
+
+def test_status_strings(L):
+    for code, name in cr.STATUS.items():
+        assert cr.convrot_status_str(code).startswith(name)
+
+
+def _weights(**kw):
+    base = dict(E=64, d=2048, I=1536, group_gu=256, group_dn=64, wbits=8, q_gu=P, s_gu=P, q_dn=P, s_dn=P)
+    base.update(kw)
+    return cr.ConvrotMoeWeightsC(*[base[f] for f, _ in cr.ConvrotMoeWeightsC._fields_])
+
+
+def test_quantize_weights_validation(L):
+    f = L.convrot_quantize_weights
+    assert f(None, 1, 1, 64, 64, 8, P, P, None) == NULL
+    assert f(P, 1, 1, 64, 64, 5, P, P, None) == BITS
+    assert f(P, 1, 1, 100, 64, 8, P, P, None) == GROUP
+    assert f(P, 1, 1, 256, 128, 8, P, P, None) == GROUP
+    assert f(P, 0, 1, 64, 64, 8, P, P, None) == SHAPE
+    assert f(P, 1, 1, 16384, 256, 8, P, P, None) == SHAPE
+    assert f(P + 2, 1, 1, 64, 64, 8, P, P, None) == ALIGN
+
+
+def test_linear_validation(L):
+    f = L.convrot_linear_w8a8
+    need = L.convrot_linear_workspace_bytes(64, 512)
+    assert need >= 64 * 512 + 64 * 4
+    assert f(P, 64, 512, P, P, 256, 64, None, P, P, need - 1, None) == WS
+    assert f(P, 64, 512, P, P, 256, 64, None, P, None, need, None) == WS
+    assert f(P, 64, 500, P, P, 256, 64, None, P, P, need, None) == GROUP
+    assert f(P, 0, 512, P, P, 256, 64, None, P, P, need, None) == SHAPE
+    assert f(P, 64, 512, None, P, 256, 64, None, P, P, need, None) == NULL
+    assert f(P, 64, 512, P, P, 256, 64, P + 8, P, P, need, None) == ALIGN
+
+
+def test_moe_forward_validation(L):
+    f = L.moe_expert_choice_forward
+    w = _weights()
+    need = L.moe_expert_choice_workspace_bytes(8192, 256, ctypes.byref(w))
+    # probs^T + slot map (E*T*4 each), qx + sx, idx + wt, a (bf16) + qa + sa, z (bf16)
+    S = 64 * 256
+    assert need >= 2 * 64 * 8192 * 4 + 8192 * 2048 + 8192 * 4 + 2 * S * 4 + S * 1536 * 3 + S * 4 + S * 2048 * 2
+    args = lambda T=8192, C=256, ww=w, ws=P, nb=need: (P, T, P, C, ctypes.byref(ww), P, None, None, ws, nb, None)
+    assert f(*args(C=8193)) == SHAPE
+    assert f(*args(C=0)) == SHAPE
+    assert f(*args(nb=need - 1)) == WS
+    assert f(*args(ww=_weights(group_gu=128))) == GROUP
+    assert f(*args(ww=_weights(d=2000))) == GROUP
+    assert f(*args(ww=_weights(wbits=3))) == BITS
+    assert f(*args(ww=_weights(q_dn=None))) == NULL
+    assert f(*args(ww=_weights(s_gu=P + 4))) == ALIGN
+    assert f(*args(ww=_weights(I=1568))) == GROUP  # 1568 is not a multiple of the down group 64
+    assert f(None, 8192, P, 256, ctypes.byref(w), P, None, None, P, need, None) == NULL
+
+
+def test_stage_validation(L):
+    assert L.convrot_rotq_rows(P, 4, 300, 64, P, P, None, None) == GROUP
+    assert L.convrot_rotq_rows(P, -1, 512, 64, P, P, None, None) == SHAPE
+    assert L.convrot_quantize_prerotated(P, 4, 12, 8, P, P, None) == SHAPE
+    assert L.convrot_quantize_prerotated(P, 4, 16, 6, P, P, None) == BITS
+    assert L.convrot_gemm_i8_i32(P, P, 4, 4, 24, P, None) == SHAPE
+    assert L.convrot_gemm_i8_i32(P, P, 4, 4, 140000, P, None) == SHAPE
+    assert L.convrot_gemm_i8_i32(P, None, 4, 4, 32, P, None) == NULL
+    nb = L.moe_route_workspace_bytes(100, 8)
+    assert nb >= 100 * 8 * 4
+    assert L.moe_route_expert_choice(P, 0, 100, 8, 101, P, P, None, P, nb, None) == SHAPE
+    assert L.moe_route_expert_choice(P, 0, 100, 8, 10, P, P, None, P, nb - 4, None) == WS
+    w = _weights()
+    assert L.moe_gateup_swiglu(P, P, 100, P, 200, ctypes.byref(w), P, None) == SHAPE
+    assert L.moe_down_proj(P, P, 0, ctypes.byref(w), P, None) == SHAPE
+    nb = L.moe_combine_workspace_bytes(100, 8)
+    assert L.moe_combine(P, P, P, 100, 8, 10, 12, P, P, nb, None) == SHAPE
+    assert L.moe_combine(P, P, P, 100, 8, 10, 64, P, P, nb - 1, None) == WS

@@ -379,3 +379,12 @@ def test_moe_close_to_unquantized_expert_choice_layer(orc, bits):
     # staged intermediates are consistent with the routing
     assert np.array_equal(r["sx"], orc.rotq_rows(x, 256)[1])
     assert r["z"].shape == (s.E * s.C, s.d)
+
+
+def test_moe_rows_equals_full_layer_at_every_token(orc):
+    s, (x, lg, w_gu, w_dn) = _small_moe(C=30)
+    q_gu, s_gu = orc.quantize_weights(w_gu, 256)
+    q_dn, s_dn = orc.quantize_weights(w_dn, 64)
+    r = orc.moe_forward(x, lg, s.C, q_gu, s_gu, 256, q_dn, s_dn, 64, intermediates=True)
+    rows = orc.moe_rows(r["qx"], r["sx"], r["idx"], r["wt"], q_gu, s_gu, q_dn, s_dn, 64, np.arange(s.T))
+    assert np.array_equal(rows, r["out"])

@@ -1,0 +1,363 @@
+// C ABI of libconvrot_amd: host-side argument validation, workspace planning and launch sequencing.
+// Every check runs before the first enqueue, so an invalid call touches no output.  The library allocates
+// no device memory; the caller passes the workspace.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/convrot.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRowLen = 8192;           // rotate/quantise keeps a row in registers of one wavefront
+constexpr int64_t kMaxKInt32 = 133144;     // K * 127^2 < 2^31
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool group_ok(int g) { return g == 64 || g == 256; }
+
+convrot_status hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_HIP; }
+
+// Carves consecutive 256-byte aligned buffers out of a workspace (or just measures when base == nullptr).
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+        used += round_up(count * sizeof(T));
+        return p;
+    }
+};
+
+struct MoeBuffers {
+    float* probs_t;
+    int32_t* slotmap;
+    int8_t* qx;
+    float* sx;
+    int32_t* idx;
+    float* wt;
+    uint16_t* a;
+    int8_t* qa;
+    float* sa;
+    uint16_t* z;
+};
+
+size_t plan_moe(void* ws, int T, int C, const convrot_moe_weights& w, MoeBuffers* b) {
+    Carver cv(ws);
+    const size_t S = (size_t)w.E * (size_t)C;
+    MoeBuffers m;
+    m.probs_t = cv.take<float>((size_t)w.E * T);
+    m.slotmap = cv.take<int32_t>((size_t)w.E * T);
+    m.qx = cv.take<int8_t>((size_t)T * w.d);
+    m.sx = cv.take<float>((size_t)T);
+    m.idx = cv.take<int32_t>(S);
+    m.wt = cv.take<float>(S);
+    m.a = cv.take<uint16_t>(S * w.I);
+    m.qa = cv.take<int8_t>(S * w.I);
+    m.sa = cv.take<float>(S);
+    m.z = cv.take<uint16_t>(S * w.d);
+    if (b) *b = m;
+    return cv.used;
+}
+
+convrot_status check_weights(const convrot_moe_weights* w) {
+    if (!w) return CONVROT_ERR_NULL;
+    if (!w->q_gu || !w->s_gu || !w->q_dn || !w->s_dn) return CONVROT_ERR_NULL;
+    if (w->E < 1 || w->d < 1 || w->I < 1) return CONVROT_ERR_SHAPE;
+    if (w->d > kMaxRowLen || w->I > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (w->wbits != 8 && w->wbits != 4) return CONVROT_ERR_BITS;
+    if (!group_ok(w->group_gu) || !group_ok(w->group_dn)) return CONVROT_ERR_GROUP;
+    if (w->d % w->group_gu || w->I % w->group_dn) return CONVROT_ERR_GROUP;
+    if (w->I % 64) return CONVROT_ERR_SHAPE;
+    if (!aligned16(w->q_gu) || !aligned16(w->s_gu) || !aligned16(w->q_dn) || !aligned16(w->s_dn))
+        return CONVROT_ERR_ALIGN;
+    if ((int64_t)w->E * 2 * w->I > INT32_MAX || (int64_t)w->E * w->d > INT32_MAX) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+convrot_status check_tc(int T, int C, int E) {
+    if (T < 1 || C < 1 || C > T || E < 1) return CONVROT_ERR_SHAPE;
+    if ((int64_t)E * C > INT32_MAX || (int64_t)E * T > INT32_MAX) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+crk::GemmProblem gateup_problem(const int8_t* qx, const float* sx, int T, const int32_t* idx, int C,
+                                const convrot_moe_weights& w, uint16_t* a) {
+    crk::GemmProblem p{};
+    p.A = qx;
+    p.a_rows = idx;
+    p.a_nrows = T;
+    p.a_scale = sx;
+    p.M = C;
+    p.B = w.q_gu;
+    p.b_scale = w.s_gu;
+    p.wbits = w.wbits;
+    p.N = 2 * w.I;
+    p.K = w.d;
+    p.E = w.E;
+    p.bias = nullptr;
+    p.out = a;
+    p.epi = crk::Epi::kSwiGLU;
+    return p;
+}
+
+crk::GemmProblem down_problem(const int8_t* qa, const float* sa, int C, const convrot_moe_weights& w,
+                              uint16_t* z) {
+    crk::GemmProblem p{};
+    p.A = qa;
+    p.a_rows = nullptr;
+    p.a_nrows = (int64_t)w.E * C;
+    p.a_scale = sa;
+    p.M = C;
+    p.B = w.q_dn;
+    p.b_scale = w.s_dn;
+    p.wbits = w.wbits;
+    p.N = w.d;
+    p.K = w.I;
+    p.E = w.E;
+    p.bias = nullptr;
+    p.out = z;
+    p.epi = crk::Epi::kBf16;
+    return p;
+}
+
+#define CRK_TRY(expr)                                   \
+    do {                                                \
+        const hipError_t crk_e_ = (expr);               \
+        if (crk_e_ != hipSuccess) return CONVROT_ERR_HIP; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* convrot_status_str(convrot_status s) {
+    switch (s) {
+        case CONVROT_OK: return "CONVROT_OK";
+        case CONVROT_ERR_NULL: return "CONVROT_ERR_NULL: required pointer is NULL";
+        case CONVROT_ERR_SHAPE: return "CONVROT_ERR_SHAPE: size out of range or inconsistent";
+        case CONVROT_ERR_GROUP: return "CONVROT_ERR_GROUP: rotation group must be 64 or 256 and divide the dimension";
+        case CONVROT_ERR_BITS: return "CONVROT_ERR_BITS: weight bits must be 8 or 4";
+        case CONVROT_ERR_ALIGN: return "CONVROT_ERR_ALIGN: pointer not 16-byte aligned";
+        case CONVROT_ERR_WORKSPACE: return "CONVROT_ERR_WORKSPACE: workspace missing or too small";
+        case CONVROT_ERR_NONFINITE: return "CONVROT_ERR_NONFINITE: non-finite weight";
+        case CONVROT_ERR_HIP: return "CONVROT_ERR_HIP: HIP launch or runtime failure";
+    }
+    return "CONVROT_ERR_UNKNOWN";
+}
+
+convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits, void* q_out,
+                                        float* scale_out, hipStream_t stream) {
+    if (!w || !q_out || !scale_out) return CONVROT_ERR_NULL;
+    if (bits != 8 && bits != 4) return CONVROT_ERR_BITS;
+    if (E < 1 || N < 1 || K < 1 || K > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
+    if (!aligned16(w) || !aligned16(q_out) || !aligned16(scale_out)) return CONVROT_ERR_ALIGN;
+    const int64_t rows = (int64_t)E * N;
+    CRK_TRY(crk::launch_rotq_weights(w, rows, K, group, bits, q_out, scale_out, stream));
+    // Rows holding NaN/Inf come back with a NaN scale; report them (the converter is offline, so it may wait).
+    std::vector<float> s((size_t)rows);
+    CRK_TRY(hipMemcpyAsync(s.data(), scale_out, sizeof(float) * (size_t)rows, hipMemcpyDeviceToHost, stream));
+    CRK_TRY(hipStreamSynchronize(stream));
+    for (float v : s)
+        if (!std::isfinite(v)) return CONVROT_ERR_NONFINITE;
+    return CONVROT_OK;
+}
+
+size_t convrot_linear_workspace_bytes(int M, int K) {
+    if (M < 1 || K < 1) return 0;
+    Carver cv(nullptr);
+    cv.take<int8_t>((size_t)M * K);
+    cv.take<float>((size_t)M);
+    return cv.used;
+}
+
+convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t* qw, const float* sw, int N,
+                                   int group, const uint16_t* bias, uint16_t* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    if (!x || !qw || !sw || !y) return CONVROT_ERR_NULL;
+    if (M < 1 || N < 1 || K < 1 || K > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y) || (bias && !aligned16(bias)))
+        return CONVROT_ERR_ALIGN;
+    if (!ws || ws_bytes < convrot_linear_workspace_bytes(M, K)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+    Carver cv(ws);
+    int8_t* qx = cv.take<int8_t>((size_t)M * K);
+    float* sx = cv.take<float>((size_t)M);
+    CRK_TRY(crk::launch_rotq_act(x, M, K, group, qx, sx, nullptr, stream));
+    crk::GemmProblem p{};
+    p.A = qx;
+    p.a_rows = nullptr;
+    p.a_nrows = M;
+    p.a_scale = sx;
+    p.M = M;
+    p.B = qw;
+    p.b_scale = sw;
+    p.wbits = 8;
+    p.N = N;
+    p.K = K;
+    p.E = 1;
+    p.bias = bias;
+    p.out = y;
+    p.epi = crk::Epi::kBf16;
+    CRK_TRY(crk::launch_grouped_gemm(p, stream));
+    return CONVROT_OK;
+}
+
+size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights* w) {
+    if (!w || T < 1 || C < 1 || w->E < 1 || w->d < 1 || w->I < 1) return 0;
+    return plan_moe(nullptr, T, C, *w, nullptr);
+}
+
+convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* router_logits, int C,
+                                         const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                         float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !router_logits || !out) return CONVROT_ERR_NULL;
+    convrot_status st = check_weights(w);
+    if (st != CONVROT_OK) return st;
+    st = check_tc(T, C, w->E);
+    if (st != CONVROT_OK) return st;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(out) || (idx_out && !aligned16(idx_out)) ||
+        (wt_out && !aligned16(wt_out)))
+        return CONVROT_ERR_ALIGN;
+    if (!ws || ws_bytes < plan_moe(nullptr, T, C, *w, nullptr)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+
+    MoeBuffers b;
+    plan_moe(ws, T, C, *w, &b);
+    int32_t* idx = idx_out ? idx_out : b.idx;
+    float* wt = wt_out ? wt_out : b.wt;
+    const int64_t S = (int64_t)w->E * C;
+
+    CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w->E, b.probs_t, nullptr, stream));
+    CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
+    CRK_TRY(crk::launch_rotq_act(x, T, w->d, w->group_gu, b.qx, b.sx, nullptr, stream));
+    CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, *w, b.a), stream));
+    CRK_TRY(crk::launch_rotq_act(b.a, S, w->I, w->group_dn, b.qa, b.sa, nullptr, stream));
+    CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, *w, b.z), stream));
+    CRK_TRY(crk::launch_combine(b.z, b.slotmap, wt, T, w->E, C, w->d, out, stream));
+    return CONVROT_OK;
+}
+
+convrot_status convrot_rotq_rows(const uint16_t* x, int64_t rows, int K, int group, int8_t* q_out, float* s_out,
+                                 float* rot_out, hipStream_t stream) {
+    if (rows < 0 || K < 1 || K > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (rows > (int64_t)4 * INT32_MAX) return CONVROT_ERR_SHAPE;
+    if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
+    if (rows == 0) return CONVROT_OK;  // nothing to do; empty buffers may be NULL
+    if (!x || !q_out || !s_out) return CONVROT_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q_out) || !aligned16(s_out) || (rot_out && !aligned16(rot_out)))
+        return CONVROT_ERR_ALIGN;
+    return hip_status(crk::launch_rotq_act(x, rows, K, group, q_out, s_out, rot_out, stream));
+}
+
+convrot_status convrot_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q_out,
+                                           float* s_out, hipStream_t stream) {
+    if (bits != 8 && bits != 4) return CONVROT_ERR_BITS;
+    if (rows < 0 || K < 8 || K > kMaxRowLen || K % 8) return CONVROT_ERR_SHAPE;
+    if (rows > (int64_t)4 * INT32_MAX) return CONVROT_ERR_SHAPE;
+    if (rows == 0) return CONVROT_OK;
+    if (!r || !q_out || !s_out) return CONVROT_ERR_NULL;
+    if (!aligned16(r) || !aligned16(q_out) || !aligned16(s_out)) return CONVROT_ERR_ALIGN;
+    return hip_status(crk::launch_quantize_prerotated(r, rows, K, bits, q_out, s_out, stream));
+}
+
+convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int N, int K, int32_t* acc_out,
+                                   hipStream_t stream) {
+    if (!a || !b || !acc_out) return CONVROT_ERR_NULL;
+    if (M < 1 || N < 1 || K < 16 || K % 16 || K > kMaxKInt32) return CONVROT_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(acc_out)) return CONVROT_ERR_ALIGN;
+    crk::GemmProblem p{};
+    p.A = a;
+    p.a_rows = nullptr;
+    p.a_nrows = M;
+    p.a_scale = nullptr;
+    p.M = M;
+    p.B = b;
+    p.b_scale = nullptr;
+    p.wbits = 8;
+    p.N = N;
+    p.K = K;
+    p.E = 1;
+    p.bias = nullptr;
+    p.out = acc_out;
+    p.epi = crk::Epi::kI32;
+    return hip_status(crk::launch_grouped_gemm(p, stream));
+}
+
+size_t moe_route_workspace_bytes(int T, int E) {
+    if (T < 1 || E < 1) return 0;
+    Carver cv(nullptr);
+    cv.take<float>((size_t)E * T);
+    return cv.used;
+}
+
+convrot_status moe_route_expert_choice(const float* in, int is_probs, int T, int E, int C, int32_t* idx_out,
+                                       float* wt_out, float* probs_out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+    if (!in || !idx_out || !wt_out) return CONVROT_ERR_NULL;
+    convrot_status st = check_tc(T, C, E);
+    if (st != CONVROT_OK) return st;
+    if (!aligned16(in) || !aligned16(idx_out) || !aligned16(wt_out) || (probs_out && !aligned16(probs_out)))
+        return CONVROT_ERR_ALIGN;
+    if (!ws || ws_bytes < moe_route_workspace_bytes(T, E)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+    float* probs_t = static_cast<float*>(ws);
+    CRK_TRY(crk::launch_softmax_t(in, is_probs ? 1 : 0, T, E, probs_t, probs_out, stream));
+    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, stream));
+    return CONVROT_OK;
+}
+
+convrot_status moe_gateup_swiglu(const int8_t* qx, const float* sx, int T, const int32_t* idx, int C,
+                                 const convrot_moe_weights* w, uint16_t* a_out, hipStream_t stream) {
+    if (!qx || !sx || !idx || !a_out) return CONVROT_ERR_NULL;
+    convrot_status st = check_weights(w);
+    if (st != CONVROT_OK) return st;
+    st = check_tc(T, C, w->E);
+    if (st != CONVROT_OK) return st;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(idx) || !aligned16(a_out)) return CONVROT_ERR_ALIGN;
+    return hip_status(crk::launch_grouped_gemm(gateup_problem(qx, sx, T, idx, C, *w, a_out), stream));
+}
+
+convrot_status moe_down_proj(const int8_t* qa, const float* sa, int C, const convrot_moe_weights* w,
+                             uint16_t* z_out, hipStream_t stream) {
+    if (!qa || !sa || !z_out) return CONVROT_ERR_NULL;
+    convrot_status st = check_weights(w);
+    if (st != CONVROT_OK) return st;
+    if (C < 1 || (int64_t)w->E * C > INT32_MAX) return CONVROT_ERR_SHAPE;
+    if (!aligned16(qa) || !aligned16(sa) || !aligned16(z_out)) return CONVROT_ERR_ALIGN;
+    return hip_status(crk::launch_grouped_gemm(down_problem(qa, sa, C, *w, z_out), stream));
+}
+
+size_t moe_combine_workspace_bytes(int T, int E) {
+    if (T < 1 || E < 1) return 0;
+    Carver cv(nullptr);
+    cv.take<int32_t>((size_t)E * T);
+    return cv.used;
+}
+
+convrot_status moe_combine(const uint16_t* z, const int32_t* idx, const float* wt, int T, int E, int C, int d,
+                           uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!z || !idx || !wt || !out) return CONVROT_ERR_NULL;
+    convrot_status st = check_tc(T, C, E);
+    if (st != CONVROT_OK) return st;
+    if (d < 8 || d % 8 || d > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (!aligned16(z) || !aligned16(idx) || !aligned16(wt) || !aligned16(out)) return CONVROT_ERR_ALIGN;
+    if (!ws || ws_bytes < moe_combine_workspace_bytes(T, E)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+    int32_t* slotmap = static_cast<int32_t*>(ws);
+    CRK_TRY(crk::launch_build_slotmap(idx, T, E, C, slotmap, stream));
+    CRK_TRY(crk::launch_combine(z, slotmap, wt, T, E, C, d, out, stream));
+    return CONVROT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Device helpers shared by the gfx950 kernels of libconvrot_amd: bf16 conversion, the fixed fp32
+// exponential, wave reductions and the XCD-aware tile mapping.
+//
+// Built with -ffp-contract=off: every fp32 expression below is evaluated as separate IEEE operations in
+// the order written, which is what makes the kernels reproducible bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crk {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+__device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t float_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// The library's fixed fp32 exponential E(x): Cody-Waite reduction x = n ln2 + r with ln2 split into a
+// 16-significant-bit head (n * head exact for |n| < 256) and an fp32 tail, e^r from the Taylor series
+// through r^7 in Horner form (coefficients 1/k! rounded to fp32), then an exact scale by 2^n.  Flushes to 0
+// below x = -86 (results under ~2^-124) and saturates to +inf above x = 88.
+__device__ __forceinline__ float exp_fixed(float x) {
+    if (x != x) return x;
+    if (x > 88.0f) return __uint_as_float(0x7f800000u);
+    if (x < -86.0f) return 0.0f;
+    const float kLog2e = 0x1.715476p+0f;
+    const float kLn2Hi = 0x1.62e4p-1f;
+    const float kLn2Lo = 0x1.7f7d1cp-20f;
+    float n = rintf(x * kLog2e);
+    float r = x - n * kLn2Hi;
+    r = r - n * kLn2Lo;
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    int ni = (int)n;
+    return p * __uint_as_float((uint32_t)(ni + 127) << 23);
+}
+
+// silu(g) = g / (1 + E(-g))
+__device__ __forceinline__ float silu_fixed(float g) {
+    float e = exp_fixed(-g);
+    float den = 1.0f + e;
+    return g / den;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m);
+    return v;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).  Remap the
+// hardware workgroup id so that each XCD receives a contiguous range of logical tiles: consecutive tiles
+// (the N-tiles of one expert) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int hw_id, int total) {
+    constexpr int kXcd = 8;
+    int xcd = hw_id % kXcd;
+    int local = hw_id / kXcd;
+    int base = total / kXcd, extra = total % kXcd;
+    int start = xcd * base + (xcd < extra ? xcd : extra);
+    return start + local;
+}
+
+}  // namespace crk

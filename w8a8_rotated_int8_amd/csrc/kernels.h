@@ -1,0 +1,55 @@
+// Internal launchers of libconvrot_amd (host side).  Arguments are validated by the C-ABI layer before any
+// of these is called; each launcher only enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace crk {
+
+// ---- rotate + quantise --------------------------------------------------------------------------------
+hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
+                           hipStream_t st);
+hipError_t launch_rotq_weights(const uint16_t* w, int64_t rows, int K, int group, int bits, void* q, float* s,
+                               hipStream_t st);
+hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,
+                                      hipStream_t st);
+
+// ---- routing ------------------------------------------------------------------------------------------
+// probs^T [E, T] from logits [T, E] (or a transpose of given probabilities); optional probs [T, E] copy.
+hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* probs_t, float* probs_out,
+                            hipStream_t st);
+// Per expert: top-C selection on probs_t[e, :]; writes idx [E, C], wt [E, C] and, if slotmap != nullptr,
+// slotmap [E, T] (position of token t in expert e's list, or -1).
+hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
+                              int32_t* slotmap, hipStream_t st);
+// slotmap [E, T] from idx [E, C].
+hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, hipStream_t st);
+
+// ---- grouped INT8 GEMM --------------------------------------------------------------------------------
+enum class Epi : int { kI32 = 0, kBf16 = 1, kSwiGLU = 2 };
+
+struct GemmProblem {
+    const int8_t* A;        // activation codes, rows of K bytes
+    const int32_t* a_rows;  // [E * M] row index into A per (expert, slot), or nullptr: row = e * M + m
+    int64_t a_nrows;        // rows of A (gathered indices are clamped into [0, a_nrows))
+    const float* a_scale;   // per A row (indexed like A), unused for kI32
+    int M;                  // rows per expert (C for the MoE, M for a plain GEMM)
+    const void* B;          // [E, N, K] int8, or [E, N, K/2] packed int4
+    const float* b_scale;   // [E, N], unused for kI32
+    int wbits;              // 8 or 4
+    int N;                  // output columns of B (2I for gate/up)
+    int K;
+    int E;
+    const uint16_t* bias;   // [N] bf16 or nullptr (kBf16 only)
+    void* out;              // kI32: int32 [E*M, N]; kBf16: bf16 [E*M, N]; kSwiGLU: bf16 [E*M, N/2]
+    Epi epi;
+};
+hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t st);
+
+// ---- combine ------------------------------------------------------------------------------------------
+hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const float* wt, int T, int E, int C, int d,
+                          uint16_t* out, hipStream_t st);
+
+}  // namespace crk

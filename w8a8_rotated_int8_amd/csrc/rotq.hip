@@ -1,0 +1,212 @@
+// Fused block-Hadamard rotation + per-row symmetric quantisation (activations and the offline weight
+// converter), and quantisation of already-rotated fp32 rows.
+//
+// ConvRot as used by the Nucleus-Image INT8 Convrot model card ("Quantization") and NitroFusion2 for
+// ComfyUI ("How they were made"): each row is rotated by the block-diagonal normalised Hadamard matrix
+// (contiguous blocks of g = 64 or 256 along K), then quantised symmetrically with one fp32 scale per row
+// (max|r| / qmax) and nearest rounding, ties to even.
+//
+// One wavefront per row.  Lane l holds the 8-element vectors i = l + 64 j (elements 8i .. 8i+7), so a
+// g-block is g/8 consecutive lanes of one j.  The fast transform runs stages h = 1, 2, 4 inside each
+// lane's vector and stages h = 8, 16, ... across lanes (partner lane l ^ (h/8)); every stage forms exactly
+// the pairs (a + b, a - b) of the textbook ascending-h transform, so the fp32 results are those of the
+// plain loop.  The row maximum is a wave reduction, the codes use IEEE division and rint.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace crk {
+namespace {
+
+struct Vec8 {
+    float v[8];
+};
+
+template <int G>
+__device__ __forceinline__ void fwht_vec_inlane(Vec8& x) {
+#pragma unroll
+    for (int h = 1; h < 8 && h < G; h *= 2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                float a = x.v[e], b = x.v[e + h];
+                x.v[e] = a + b;
+                x.v[e + h] = a - b;
+            }
+}
+
+// Stages h = 8m for m = 1, 2, ..., g/16: the partner of element (lane, e) is (lane ^ m, e); the lane
+// holding the lower index keeps a + b, the other keeps a - b.
+template <int G>
+__device__ __forceinline__ void fwht_vec_crosslane(Vec8& x, int lane) {
+#pragma unroll
+    for (int m = 1; m < G / 8; m *= 2) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float mine = x.v[e];
+            float other = __shfl_xor(mine, m);
+            x.v[e] = upper ? (other - mine) : (mine + other);
+        }
+    }
+}
+
+// One quantised code: clamp(rint(r / scale), -qmax, qmax), or 0 if scale == 0.
+template <int QMAX>
+__device__ __forceinline__ int quant_code(float r, float scale) {
+    if (scale == 0.0f) return 0;
+    float c = rintf(r / scale);
+    c = fminf(fmaxf(c, -(float)QMAX), (float)QMAX);
+    return (int)c;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// G: rotation group (0 = no rotation, fp32 input); NV: vectors per lane (K <= 512 NV);
+// QMAX: 127 or 7; PACK4: write nibble-packed int4 codes; CHECK: flag non-finite rows with a NaN scale.
+template <int G, int NV, int QMAX, bool PACK4, bool CHECK>
+__global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__ xin, int64_t rows, int K,
+                                                        void* __restrict__ qout, float* __restrict__ sout,
+                                                        float* __restrict__ rot_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const int nvec = K >> 3;
+
+    Vec8 x[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i < nvec) {
+            if constexpr (G > 0) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(
+                    static_cast<const uint16_t*>(xin) + row * (int64_t)K + 8 * i);
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[j].v[2 * e] = bf16_to_float(w[e] & 0xffffu);
+                    x[j].v[2 * e + 1] = bf16_to_float(w[e] >> 16);
+                }
+            } else {
+                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xin) +
+                                                                  row * (int64_t)K + 8 * i);
+                const float4 a = p[0], b = p[1];
+                x[j].v[0] = a.x; x[j].v[1] = a.y; x[j].v[2] = a.z; x[j].v[3] = a.w;
+                x[j].v[4] = b.x; x[j].v[5] = b.y; x[j].v[6] = b.z; x[j].v[7] = b.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[j].v[e] = 0.0f;
+        }
+    }
+
+    if constexpr (G > 0) {
+        constexpr float kNorm = (G == 256) ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            fwht_vec_inlane<G>(x[j]);
+            fwht_vec_crosslane<G>(x[j], lane);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[j].v[e] = x[j].v[e] * kNorm;
+        }
+    }
+
+    float amax = 0.0f;
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float a = fabsf(x[j].v[e]);
+            amax = fmaxf(amax, a);
+            if constexpr (CHECK) bad |= !(a <= 3.40282347e38f);
+        }
+    amax = wave_max(amax);
+    float scale = amax / (float)QMAX;
+    if constexpr (CHECK) {
+        if (wave_or(bad)) scale = __uint_as_float(0x7fc00000u);
+    }
+
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i >= nvec) continue;
+        int c[8];
+        if (CHECK && scale != scale) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[e] = 0;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[e] = quant_code<QMAX>(x[j].v[e], scale);
+        }
+        if constexpr (PACK4) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) packed |= (uint32_t)(c[e] & 0xf) << (4 * e);
+            *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(qout) + row * (int64_t)(K / 2) + 4 * i) = packed;
+        } else {
+            uint2 o;
+            o.x = pack4_i8(c[0], c[1], c[2], c[3]);
+            o.y = pack4_i8(c[4], c[5], c[6], c[7]);
+            *reinterpret_cast<uint2*>(static_cast<int8_t*>(qout) + row * (int64_t)K + 8 * i) = o;
+        }
+        if (rot_out) {
+            float4* r = reinterpret_cast<float4*>(rot_out + row * (int64_t)K + 8 * i);
+            r[0] = make_float4(x[j].v[0], x[j].v[1], x[j].v[2], x[j].v[3]);
+            r[1] = make_float4(x[j].v[4], x[j].v[5], x[j].v[6], x[j].v[7]);
+        }
+    }
+    if (lane == 0) sout[row] = scale;
+}
+
+template <int G, int QMAX, bool PACK4, bool CHECK>
+hipError_t launch_nv(const void* x, int64_t rows, int K, void* q, float* s, float* rot, hipStream_t st) {
+    const int nv = (K / 8 + 63) / 64;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+#define CRK_NV_CASE(N)                                                                                   \
+    if (nv <= N) {                                                                                       \
+        rotq_rows_kernel<G, N, QMAX, PACK4, CHECK><<<grid, block, 0, st>>>(x, rows, K, q, s, rot);       \
+        return hipGetLastError();                                                                        \
+    }
+    CRK_NV_CASE(1)
+    CRK_NV_CASE(2)
+    CRK_NV_CASE(3)
+    CRK_NV_CASE(4)
+    CRK_NV_CASE(6)
+    CRK_NV_CASE(8)
+    CRK_NV_CASE(12)
+    CRK_NV_CASE(16)
+#undef CRK_NV_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
+                           hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (group == 256) return launch_nv<256, 127, false, false>(x, rows, K, q, s, rot, st);
+    return launch_nv<64, 127, false, false>(x, rows, K, q, s, rot, st);
+}
+
+hipError_t launch_rotq_weights(const uint16_t* w, int64_t rows, int K, int group, int bits, void* q, float* s,
+                               hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (bits == 8) {
+        if (group == 256) return launch_nv<256, 127, false, true>(w, rows, K, q, s, nullptr, st);
+        return launch_nv<64, 127, false, true>(w, rows, K, q, s, nullptr, st);
+    }
+    if (group == 256) return launch_nv<256, 7, true, true>(w, rows, K, q, s, nullptr, st);
+    return launch_nv<64, 7, true, true>(w, rows, K, q, s, nullptr, st);
+}
+
+hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,
+                                      hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (bits == 8) return launch_nv<0, 127, false, false>(r, rows, K, q, s, nullptr, st);
+    return launch_nv<0, 7, false, false>(r, rows, K, q, s, nullptr, st);
+}
+
+}  // namespace crk
