@@ -28,11 +28,11 @@
  *    lower token index, listed in ascending token order; its gate weight is that p (not renormalised).
  *  - Combine: out[t, :] = bf16_rne( sum over experts e in ascending order that took t of w * (float)z ),
  *    fp32, starting from +0.0f; a token taken by no expert gets +0.
- *  - E(x) is a fixed fp32 exponential: n = rint(x * log2e), r = (x - n*ln2_hi) - n*ln2_lo with ln2_hi = ln 2
- *    rounded to 16 significant bits (Cody-Waite reduction), Taylor series of e^r through r^7 in Horner form
- *    (coefficients 1/k! rounded to fp32), scaled by 2^n; E(x) = 0 for x < -86 and +inf for x > 88.  Every
- *    fp32 step above is a separate IEEE operation (no fused multiply-add), so results are reproducible
- *    bit for bit.
+ *  - E(x) is a fixed fp32 exponential: x clamped to [-86, 88]; n = rint(x * log2e); r = fma(-n, ln2_lo,
+ *    fma(-n, ln2_hi, x)) with ln2_hi = ln 2 rounded to 16 significant bits (Cody-Waite reduction); Taylor
+ *    series of e^r through r^7 by Horner's rule in fused multiply-adds (coefficients 1/k! rounded to fp32);
+ *    exact scaling by 2^n.  Every other fp32 step above is a separate IEEE operation (no contraction), so
+ *    results are reproducible bit for bit.
  *
  * Conventions for every call:
  *  - Pointers marked (device) are device memory on the current HIP device; bf16 crosses the ABI as raw
@@ -71,7 +71,25 @@ typedef enum convrot_status {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* convrot_status_str(convrot_status s);
 
-/* Quantised weights of one routed-expert MoE layer.  The struct itself lives in host memory. */
+/* Layouts of quantised weight codes.
+ *  CONVROT_LAYOUT_ROWMAJOR: codes of row n, column k at byte n*K + k (int8), or nibble k%2 of byte
+ *    n*(K/2) + k/2 (int4; even k in bits 0-3).  Interchange / inspection format.
+ *  CONVROT_LAYOUT_MFMA: the format the GEMMs stream.  Rows are grouped in blocks of 32 (NB = ceil(N/32)
+ *    blocks, rows past N are zero); every (row block nb, K-block) is one contiguous 1 KiB tile laid out in
+ *    the lane order of the gfx950 v_mfma_i32_32x32x32_i8 B operand, so that a wavefront fetches it with one
+ *    coalesced 16-byte load per lane.  With r = n % 32:
+ *      int8 (K-blocks of 32):  byte ((nb*(K/32) + k/32)*1024 + (r + 32*((k%32)/16))*16 + k%16)
+ *      int4 (K-blocks of 64):  byte ((nb*(K/64) + k/64)*1024 + (r + 32*((k%32)/16))*16 + 8*((k%64)/32)
+ *                                    + (k%16)/2), nibble k%2 (even k in bits 0-3); requires K % 64 == 0.
+ *    For [E, N, K] weights expert e starts at byte e * NB * K (int8) or e * NB * K / 2 (int4), i.e. the
+ *    buffer holds E * NB * 32 * K (or half that) bytes. */
+typedef enum convrot_layout { CONVROT_LAYOUT_ROWMAJOR = 0, CONVROT_LAYOUT_MFMA = 1 } convrot_layout;
+
+/* Bytes of a quantised [E, N, K] weight tensor in the given layout and bit width. */
+size_t convrot_weight_bytes(int E, int N, int K, int bits, int layout);
+
+/* Quantised weights of one routed-expert MoE layer.  The struct itself lives in host memory.  Codes are in
+ * CONVROT_LAYOUT_MFMA. */
 typedef struct convrot_moe_weights {
     int E;             /* routed experts, >= 1 */
     int d;             /* model width (gate/up input, down output), multiple of group_gu */
@@ -79,9 +97,9 @@ typedef struct convrot_moe_weights {
     int group_gu;      /* rotation group of gate/up: 64 or 256 (the pages use 256) */
     int group_dn;      /* rotation group of down: 64 or 256 (the pages use 64) */
     int wbits;         /* 8: int8 codes; 4: nibble-packed int4 codes (even k in bits 0-3) */
-    const void* q_gu;  /* (device) [E, 2I, d] int8, or [E, 2I, d/2] u8; rows 0..I-1 gate, I..2I-1 up */
+    const void* q_gu;  /* (device) [E, 2I, d] codes, MFMA layout; rows 0..I-1 gate, I..2I-1 up */
     const float* s_gu; /* (device) [E, 2I] fp32 per-output-row scales */
-    const void* q_dn;  /* (device) [E, d, I] int8, or [E, d, I/2] u8 */
+    const void* q_dn;  /* (device) [E, d, I] codes, MFMA layout */
     const float* s_dn; /* (device) [E, d] fp32 */
 } convrot_moe_weights;
 
@@ -89,12 +107,12 @@ typedef struct convrot_moe_weights {
 /* Offline weight converter  (model card "Quantization": rotate each expert matrix, quantise per row)     */
 /* ---------------------------------------------------------------------------------------------------- */
 
-/* w (device) [E, N, K] bf16 -> q_out (device) int8 [E, N, K] (bits = 8) or u8 [E, N, K/2] (bits = 4), and
- * scale_out (device) [E, N] fp32.  Each row is rotated along K in blocks of `group` and quantised with its
- * own scale (qmax 127 or 7).  Requires E, N >= 1, 1 <= K <= 8192, K % group == 0.  A non-finite weight
- * makes the call return CONVROT_ERR_NONFINITE after the stream work completes (this call synchronises
- * `stream`); outputs are then unspecified. */
-convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits,
+/* w (device) [E, N, K] bf16 -> q_out (device, convrot_weight_bytes(E, N, K, bits, layout) bytes) codes in
+ * `layout`, and scale_out (device) [E, N] fp32.  Each row is rotated along K in blocks of `group` and
+ * quantised with its own scale (qmax 127 for bits = 8, 7 for bits = 4).  Requires E, N >= 1,
+ * 1 <= K <= 8192, K % group == 0.  A non-finite weight makes the call return CONVROT_ERR_NONFINITE after
+ * the stream work completes (this call synchronises `stream`); outputs are then unspecified. */
+convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits, int layout,
                                         void* q_out, float* scale_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------------- */
@@ -105,7 +123,8 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
 size_t convrot_linear_workspace_bytes(int M, int K);
 
 /* y[M, N] = bf16( ((float)(rotq(x) . qw^T) * sx) * sw ) (+ bias).  x (device) [M, K] bf16; qw (device)
- * [N, K] int8 from convrot_quantize_weights with the same group; sw (device) [N]; bias (device) [N] bf16
+ * [N, K] int8 codes in CONVROT_LAYOUT_MFMA from convrot_quantize_weights with the same group; sw (device)
+ * [N]; bias (device) [N] bf16
  * or NULL; y (device) [M, N] bf16; ws (device) at least convrot_linear_workspace_bytes(M, K).
  * Requires M, N >= 1, K <= 8192, K % group == 0, group 64 or 256. */
 convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t* qw, const float* sw, int N,
@@ -148,8 +167,9 @@ convrot_status convrot_rotq_rows(const uint16_t* x, int64_t rows, int K, int gro
 convrot_status convrot_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q_out,
                                            float* s_out, hipStream_t stream);
 
-/* acc_out[M, N] = a[M, K] . b[N, K]^T exactly in int32, with the same INT8 MFMA main loop as the layer.
- * Requires M, N >= 1, 16 <= K <= 133144, K % 16 == 0. */
+/* acc_out[M, N] = a[M, K] . b[N, K]^T exactly in int32 (both row-major int8), with the same INT8 MFMA main
+ * loop as the layer (B fetched row-major instead of tiled).  Requires M, N >= 1, 16 <= K <= 133144,
+ * K % 16 == 0. */
 convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int N, int K, int32_t* acc_out,
                                    hipStream_t stream);
 

@@ -34,7 +34,8 @@
  *    (fp32 division, ties to even); an all-zero row has scale 0 and codes 0.  qmax = 127 for INT8,
  *    7 for INT4.  Activations use one scale per token over the whole rotated row.
  *  - Dequantisation: bf16( ((float)acc * s_act) * s_w ), optional bias added in fp32 before rounding.
- *  - silu(g) = g / (1 + E(-g)), where E is the fixed fp32 exponential defined in oracle_exp below.
+ *  - silu(g) = g / (1 + E(-g)), where E is the fixed fp32 exponential defined in oracle_exp below
+ *    (clamped argument, Cody-Waite reduction, Taylor polynomial, fused multiply-adds as written).
  *  - Router: softmax over the experts of each token in fp32 (max-subtracted, E() of the differences,
  *    sum in ascending expert order, one division).  Expert e takes the C tokens with the largest
  *    probability, ties to the lower token index; its list is written in ascending token order and its
@@ -75,37 +76,34 @@ void oracle_bf16_round(const float* in, int64_t n, uint16_t* out) {
 /* ------------------------------------------------------------------------------------------------- */
 /* E(x): the fixed fp32 exponential used by silu and softmax.                                          */
 /*                                                                                                     */
-/* Cody & Waite's additive range reduction ("Software Manual for the Elementary Functions", 1980):    */
-/* n = rint(x * log2(e)), r = (x - n*LN2_HI) - n*LN2_LO, where LN2_HI is ln 2 rounded to 16            */
-/* significant bits (so n*LN2_HI is exact for |n| < 256) and LN2_LO = ln 2 - LN2_HI rounded to fp32;  */
-/* then e^r by its Taylor series through r^7 (terms 1/k! rounded to fp32) in Horner form, and the     */
-/* result scaled by 2^n.  Results below about 2^-124 are flushed to +0 (x < -86), results above 2^127  */
-/* saturate to +inf (x > 88).  Every operation is a separate, correctly rounded fp32 operation.        */
+/* The argument is first clamped to [-86, 88] (outside, E returns the value at the end of the range:   */
+/* about 4.5e-38 below, 1.65e38 above).  Then Cody & Waite's additive range reduction ("Software       */
+/* Manual for the Elementary Functions", 1980): n = rint(x * log2(e)), r = x - n*LN2_HI - n*LN2_LO,     */
+/* where LN2_HI is ln 2 rounded to 16 significant bits (n*LN2_HI is exact for |n| < 256) and LN2_LO =  */
+/* ln 2 - LN2_HI rounded to fp32, each step one fused multiply-add.  e^r comes from its Taylor series   */
+/* through r^7 (terms 1/k! rounded to fp32) evaluated by Horner's rule with fused multiply-adds, and    */
+/* the result is scaled exactly by 2^n.  fmaf and ldexpf are correctly rounded / exact, so this is a   */
+/* fixed sequence of IEEE fp32 operations.                                                             */
 /* ------------------------------------------------------------------------------------------------- */
 
 float oracle_exp(float x) {
-    if (x != x) return x;
-    if (x > 88.0f) return INFINITY;
-    if (x < -86.0f) return 0.0f;
     const float log2e = 0x1.715476p+0f;       /* log2(e) rounded to fp32 */
     const float ln2_hi = 0x1.62e4p-1f;        /* 45426 / 65536 = 0.693145751953125 */
     const float ln2_lo = 0x1.7f7d1cp-20f;     /* ln 2 - ln2_hi, rounded to fp32 */
+    if (x < -86.0f) x = -86.0f;
+    if (x > 88.0f) x = 88.0f;
     float n = rintf(x * log2e);
-    float r = x - n * ln2_hi;
-    r = r - n * ln2_lo;
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
     float p = 1.0f / 5040.0f;                 /* 1/7! */
-    p = p * r + 1.0f / 720.0f;
-    p = p * r + 1.0f / 120.0f;
-    p = p * r + 1.0f / 24.0f;
-    p = p * r + 1.0f / 6.0f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
-    int ni = (int)n; /* -124 <= n <= 127 on the kept range */
-    uint32_t bits = (uint32_t)(ni + 127) << 23;
-    float scale;
-    memcpy(&scale, &bits, sizeof scale);
-    return p * scale;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)n); /* -124 <= n <= 127: a normal result, exact scaling */
 }
 
 void oracle_exp_array(const float* x, int64_t n, float* out) {

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
@@ -36,13 +36,19 @@ def _weights(**kw):
 
 def test_quantize_weights_validation(L):
     f = L.convrot_quantize_weights
-    assert f(None, 1, 1, 64, 64, 8, P, P, None) == NULL
-    assert f(P, 1, 1, 64, 64, 5, P, P, None) == BITS
-    assert f(P, 1, 1, 100, 64, 8, P, P, None) == GROUP
-    assert f(P, 1, 1, 256, 128, 8, P, P, None) == GROUP
-    assert f(P, 0, 1, 64, 64, 8, P, P, None) == SHAPE
-    assert f(P, 1, 1, 16384, 256, 8, P, P, None) == SHAPE
-    assert f(P + 2, 1, 1, 64, 64, 8, P, P, None) == ALIGN
+    assert f(None, 1, 1, 64, 64, 8, 1, P, P, None) == NULL
+    assert f(P, 1, 1, 64, 64, 5, 1, P, P, None) == BITS
+    assert f(P, 1, 1, 100, 64, 8, 1, P, P, None) == GROUP
+    assert f(P, 1, 1, 256, 128, 8, 0, P, P, None) == GROUP
+    assert f(P, 0, 1, 64, 64, 8, 1, P, P, None) == SHAPE
+    assert f(P, 1, 1, 16384, 256, 8, 1, P, P, None) == SHAPE
+    assert f(P, 1, 1, 256, 256, 8, 2, P, P, None) == SHAPE
+    assert f(P + 2, 1, 1, 64, 64, 8, 1, P, P, None) == ALIGN
+    # MFMA layout pads rows to blocks of 32; int4 halves the bytes
+    assert L.convrot_weight_bytes(64, 3072, 2048, 8, 1) == 64 * 3072 * 2048
+    assert L.convrot_weight_bytes(2, 33, 512, 8, 1) == 2 * 64 * 512
+    assert L.convrot_weight_bytes(2, 33, 512, 4, 1) == 2 * 64 * 256
+    assert L.convrot_weight_bytes(2, 33, 512, 8, 0) == 2 * 33 * 512
 
 
 def test_linear_validation(L):

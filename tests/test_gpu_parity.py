@@ -12,7 +12,7 @@ import oracle
 from w8a8_rotated_int8_amd import binding as cr
 from w8a8_rotated_int8_amd import synth
 
-from helpers import DEV, assert_bf16_within, dev, dev_bf16, host, host_bf16, say
+from helpers import DEV, assert_bf16_within, dev, dev_bf16, host, host_bf16, say, untile_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -117,14 +117,24 @@ def test_quantize_prerotated_ties_and_subnormals():
 # ----------------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("g,shape", [(64, (3, 40, 512)), (256, (2, 33, 1536)), (64, (1, 5, 8192))])
+@pytest.mark.parametrize("g,shape", [(64, (3, 40, 512)), (256, (2, 33, 1536)), (64, (1, 5, 8192)), (256, (2, 64, 256))])
 def test_weight_converter_bit_exact(bits, g, shape):
     say(f"convert bits={bits} g={g} shape={shape}")
     w = synth.weights(900 + g + bits, shape)
-    q, s = cr.convrot_quantize_weights(dev_bf16(w), g, bits)
     rq, rs = oracle.quantize_weights(w, g, bits)
+    q, s = cr.convrot_quantize_weights(dev_bf16(w), g, bits, layout=cr.LAYOUT_ROWMAJOR)
     assert np.array_equal(host(q), rq)
     assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    qt, st = cr.convrot_quantize_weights(dev_bf16(w), g, bits, layout=cr.LAYOUT_MFMA)
+    E, N, K = shape
+    assert qt.numel() == cr.convrot_weight_bytes(E, N, K, bits, cr.LAYOUT_MFMA) == E * ((N + 31) // 32) * 32 * K * bits // 8
+    codes = rq if bits == 8 else oracle.unpack_int4(rq, K)
+    assert np.array_equal(untile_codes(host(qt), E, N, K, bits), codes)
+    # rows past N in the last block are zero
+    NB = (N + 31) // 32
+    full = untile_codes(host(qt), E, NB * 32, K, bits)
+    assert not full[:, N:, :].any()
+    assert np.array_equal(host(st).view(np.uint32), rs.view(np.uint32))
 
 
 def test_weight_converter_rejects_nonfinite():
@@ -203,7 +213,10 @@ def _layer(shape, bits, seed):
     ref = oracle.moe_forward(x, lg, shape.C, q_gu, s_gu, shape.g_gu, q_dn, s_dn, shape.g_dn, bits,
                              intermediates=True)
     w = cr.quantize_moe_weights(dev_bf16(w_gu), dev_bf16(w_dn), shape.g_gu, shape.g_dn, bits)
-    assert np.array_equal(host(w.q_gu), q_gu) and np.array_equal(host(w.q_dn), q_dn)
+    cg = q_gu if bits == 8 else oracle.unpack_int4(q_gu, shape.d)
+    cd = q_dn if bits == 8 else oracle.unpack_int4(q_dn, shape.I)
+    assert np.array_equal(untile_codes(host(w.q_gu), shape.E, 2 * shape.I, shape.d, bits), cg)
+    assert np.array_equal(untile_codes(host(w.q_dn), shape.E, shape.d, shape.I, bits), cd)
     return x, lg, w, ref
 
 
@@ -250,7 +263,8 @@ def test_single_expert_ffn_config1():
     out, idx, wt = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w)
     q_gu, s_gu = oracle.quantize_weights(w_gu, 256)
     q_dn, s_dn = oracle.quantize_weights(w_dn, 64)
-    assert np.array_equal(host(w.q_gu), q_gu) and np.array_equal(host(w.s_dn), s_dn)
+    assert np.array_equal(untile_codes(host(w.q_gu), 1, 3072, 2048, 8), q_gu)
+    assert np.array_equal(host(w.s_dn), s_dn)
     ref = oracle.moe_forward(x, lg, shape.C, q_gu, s_gu, 256, q_dn, s_dn, 64)
     assert np.array_equal(host(idx), ref["idx"]) and np.all(host(wt) == 1.0)
     exact = assert_bf16_within(host_bf16(out), ref["out"], what="config 1 out")

@@ -40,7 +40,8 @@ class ConvrotMoeWeightsC(ctypes.Structure):
 _p, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "convrot_status_str": (ctypes.c_char_p, [_i]),
-    "convrot_quantize_weights": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "convrot_weight_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "convrot_quantize_weights": (_i, [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "convrot_linear_workspace_bytes": (_sz, [_i, _i]),
     "convrot_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
     "moe_expert_choice_workspace_bytes": (_sz, [_i, _i, ctypes.POINTER(ConvrotMoeWeightsC)]),
@@ -141,16 +142,28 @@ def convrot_status_str(status: int) -> str:
     return lib().convrot_status_str(status).decode()
 
 
-def convrot_quantize_weights(w: torch.Tensor, group: int, bits: int = 8, q_out=None, scale_out=None, stream=None):
-    """w [E, N, K] (or [N, K]) bf16 -> (codes int8 [.., K] or packed uint8 [.., K/2], scales fp32 [.., N])."""
+LAYOUT_ROWMAJOR, LAYOUT_MFMA = 0, 1
+
+
+def convrot_weight_bytes(E: int, N: int, K: int, bits: int = 8, layout: int = LAYOUT_MFMA) -> int:
+    return lib().convrot_weight_bytes(E, N, K, bits, layout)
+
+
+def convrot_quantize_weights(w: torch.Tensor, group: int, bits: int = 8, layout: int = LAYOUT_MFMA, q_out=None,
+                             scale_out=None, stream=None):
+    """w [E, N, K] (or [N, K]) bf16 -> (codes as a flat uint8/int8 buffer in `layout`, scales fp32 [.., N]).
+    Row-major codes come back shaped [.., N, K] (int8) or [.., N, K/2] (uint8, packed int4)."""
     shape = w.shape
     E, N, K = (1, *shape) if w.dim() == 2 else shape
     if q_out is None:
-        q_out = _empty((*shape[:-1], K if bits == 8 else K // 2), torch.int8 if bits == 8 else torch.uint8, w)
+        if layout == LAYOUT_ROWMAJOR:
+            q_out = _empty((*shape[:-1], K if bits == 8 else K // 2), torch.int8 if bits == 8 else torch.uint8, w)
+        else:
+            q_out = _empty((convrot_weight_bytes(E, N, K, bits, layout),), torch.int8 if bits == 8 else torch.uint8, w)
     if scale_out is None:
         scale_out = _empty(shape[:-1], torch.float32, w)
     _check("convrot_quantize_weights", lib().convrot_quantize_weights(
-        _ptr(w), E, N, K, group, bits, _ptr(q_out), _ptr(scale_out), _stream(stream)))
+        _ptr(w), E, N, K, group, bits, layout, _ptr(q_out), _ptr(scale_out), _stream(stream)))
     return q_out, scale_out
 
 
@@ -172,8 +185,9 @@ def convrot_linear_workspace_bytes(M: int, K: int) -> int:
 
 
 def convrot_linear_w8a8(x, qw, sw, group: int, bias=None, y=None, ws=None, stream=None):
+    """qw: codes in the MFMA layout (from convrot_quantize_weights); N is taken from the scales sw [N]."""
     M, K = x.shape
-    N = qw.shape[0]
+    N = sw.shape[0]
     if y is None:
         y = _empty((M, N), torch.bfloat16, x)
     nbytes = convrot_linear_workspace_bytes(M, K)

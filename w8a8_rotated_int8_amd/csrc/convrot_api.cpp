@@ -98,6 +98,7 @@ crk::GemmProblem gateup_problem(const int8_t* qx, const float* sx, int T, const 
     p.a_scale = sx;
     p.M = C;
     p.B = w.q_gu;
+    p.b_tiled = true;
     p.b_scale = w.s_gu;
     p.wbits = w.wbits;
     p.N = 2 * w.I;
@@ -118,6 +119,7 @@ crk::GemmProblem down_problem(const int8_t* qa, const float* sa, int C, const co
     p.a_scale = sa;
     p.M = C;
     p.B = w.q_dn;
+    p.b_tiled = true;
     p.b_scale = w.s_dn;
     p.wbits = w.wbits;
     p.N = w.d;
@@ -154,15 +156,24 @@ const char* convrot_status_str(convrot_status s) {
     return "CONVROT_ERR_UNKNOWN";
 }
 
-convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits, void* q_out,
-                                        float* scale_out, hipStream_t stream) {
+size_t convrot_weight_bytes(int E, int N, int K, int bits, int layout) {
+    if (E < 1 || N < 1 || K < 1 || (bits != 8 && bits != 4)) return 0;
+    const size_t rows = layout == CONVROT_LAYOUT_MFMA ? (size_t)((N + 31) / 32) * 32 : (size_t)N;
+    return (size_t)E * rows * (size_t)K * (size_t)bits / 8;
+}
+
+convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, int group, int bits, int layout,
+                                        void* q_out, float* scale_out, hipStream_t stream) {
     if (!w || !q_out || !scale_out) return CONVROT_ERR_NULL;
     if (bits != 8 && bits != 4) return CONVROT_ERR_BITS;
+    if (layout != CONVROT_LAYOUT_ROWMAJOR && layout != CONVROT_LAYOUT_MFMA) return CONVROT_ERR_SHAPE;
     if (E < 1 || N < 1 || K < 1 || K > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if ((int64_t)E * ((N + 31) / 32) * 32 > (int64_t)4 * INT32_MAX) return CONVROT_ERR_SHAPE;
     if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
     if (!aligned16(w) || !aligned16(q_out) || !aligned16(scale_out)) return CONVROT_ERR_ALIGN;
     const int64_t rows = (int64_t)E * N;
-    CRK_TRY(crk::launch_rotq_weights(w, rows, K, group, bits, q_out, scale_out, stream));
+    CRK_TRY(crk::launch_rotq_weights(w, E, N, K, group, bits, layout == CONVROT_LAYOUT_MFMA, q_out, scale_out,
+                                     stream));
     // Rows holding NaN/Inf come back with a NaN scale; report them (the converter is offline, so it may wait).
     std::vector<float> s((size_t)rows);
     CRK_TRY(hipMemcpyAsync(s.data(), scale_out, sizeof(float) * (size_t)rows, hipMemcpyDeviceToHost, stream));
@@ -201,6 +212,7 @@ convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t
     p.a_scale = sx;
     p.M = M;
     p.B = qw;
+    p.b_tiled = true;
     p.b_scale = sw;
     p.wbits = 8;
     p.N = N;
@@ -283,6 +295,7 @@ convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int 
     p.a_scale = nullptr;
     p.M = M;
     p.B = b;
+    p.b_tiled = false;
     p.b_scale = nullptr;
     p.wbits = 8;
     p.N = N;

@@ -2,7 +2,8 @@
 // exponential, wave reductions and the XCD-aware tile mapping.
 //
 // Built with -ffp-contract=off: every fp32 expression below is evaluated as separate IEEE operations in
-// the order written, which is what makes the kernels reproducible bit for bit.
+// the order written (fused multiply-adds only where written explicitly), which is what makes the kernels
+// reproducible bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,38 +15,32 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN.
+// fp32 -> bf16 bits, round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t float_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// The library's fixed fp32 exponential E(x): Cody-Waite reduction x = n ln2 + r with ln2 split into a
-// 16-significant-bit head (n * head exact for |n| < 256) and an fp32 tail, e^r from the Taylor series
-// through r^7 in Horner form (coefficients 1/k! rounded to fp32), then an exact scale by 2^n.  Flushes to 0
-// below x = -86 (results under ~2^-124) and saturates to +inf above x = 88.
+// The library's fixed fp32 exponential E(x).  The argument is clamped to [-86, 88]; then Cody-Waite
+// reduction x = n ln2 + r with ln2 split into a 16-significant-bit head (n * head exact for |n| < 256) and an
+// fp32 tail (one fused multiply-add each), e^r from the Taylor series through r^7 (coefficients 1/k! rounded to
+// fp32) by Horner's rule in fused multiply-adds, and an exact scale by 2^n (v_ldexp_f32).
 __device__ __forceinline__ float exp_fixed(float x) {
-    if (x != x) return x;
-    if (x > 88.0f) return __uint_as_float(0x7f800000u);
-    if (x < -86.0f) return 0.0f;
     const float kLog2e = 0x1.715476p+0f;
     const float kLn2Hi = 0x1.62e4p-1f;
     const float kLn2Lo = 0x1.7f7d1cp-20f;
-    float n = rintf(x * kLog2e);
-    float r = x - n * kLn2Hi;
-    r = r - n * kLn2Lo;
+    x = __builtin_amdgcn_fmed3f(x, -86.0f, 88.0f);
+    const float n = rintf(x * kLog2e);
+    float r = __builtin_fmaf(-n, kLn2Hi, x);
+    r = __builtin_fmaf(-n, kLn2Lo, r);
     float p = 1.0f / 5040.0f;
-    p = p * r + 1.0f / 720.0f;
-    p = p * r + 1.0f / 120.0f;
-    p = p * r + 1.0f / 24.0f;
-    p = p * r + 1.0f / 6.0f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
-    int ni = (int)n;
-    return p * __uint_as_float((uint32_t)(ni + 127) << 23);
+    p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_amdgcn_ldexpf(p, (int)n);
 }
 
 // silu(g) = g / (1 + E(-g))

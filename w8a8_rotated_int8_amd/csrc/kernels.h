@@ -11,8 +11,9 @@ namespace crk {
 // ---- rotate + quantise --------------------------------------------------------------------------------
 hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
                            hipStream_t st);
-hipError_t launch_rotq_weights(const uint16_t* w, int64_t rows, int K, int group, int bits, void* q, float* s,
-                               hipStream_t st);
+// Weights [E, N, K]: row-major codes, or the MFMA-tiled layout when `tiled` (rows padded to blocks of 32).
+hipError_t launch_rotq_weights(const uint16_t* w, int E, int N, int K, int group, int bits, bool tiled, void* q,
+                               float* s, hipStream_t st);
 hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,
                                       hipStream_t st);
 
@@ -36,7 +37,8 @@ struct GemmProblem {
     int64_t a_nrows;        // rows of A (gathered indices are clamped into [0, a_nrows))
     const float* a_scale;   // per A row (indexed like A), unused for kI32
     int M;                  // rows per expert (C for the MoE, M for a plain GEMM)
-    const void* B;          // [E, N, K] int8, or [E, N, K/2] packed int4
+    const void* B;          // [E, N, K] codes: MFMA-tiled (b_tiled, int8 or int4) or row-major int8
+    bool b_tiled;
     const float* b_scale;   // [E, N], unused for kI32
     int wbits;              // 8 or 4
     int N;                  // output columns of B (2I for gate/up)

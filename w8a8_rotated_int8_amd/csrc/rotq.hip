@@ -64,22 +64,55 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
+// Byte offset of the 8 codes k = 8i .. 8i+7 of row n (of one expert) in the MFMA-tiled layout: every
+// (32-row block, K-block) tile is 1 KiB in the lane order of the v_mfma_i32_32x32x32_i8 B operand (lane
+// r + 32*((k%32)/16) holds 16 consecutive k); int4 tiles span 64 k and hold two 8-byte halves per lane.
+template <bool INT4>
+__device__ __forceinline__ int64_t tiled_offset(int n, int k, int K) {
+    const int r = n & 31, lane = r + 32 * ((k & 31) >> 4);
+    if constexpr (!INT4) {
+        return ((int64_t)(n >> 5) * (K >> 5) + (k >> 5)) * 1024 + lane * 16 + (k & 15);
+    } else {
+        return ((int64_t)(n >> 5) * (K >> 6) + (k >> 6)) * 1024 + lane * 16 + 8 * ((k & 63) >> 5) + ((k & 15) >> 1);
+    }
+}
+
+// Output modes of the codes.
+enum class Out : int { kRowI8 = 0, kRowI4 = 1, kTiledI8 = 2, kTiledI4 = 3 };
+
 // G: rotation group (0 = no rotation, fp32 input); NV: vectors per lane (K <= 512 NV);
-// QMAX: 127 or 7; PACK4: write nibble-packed int4 codes; CHECK: flag non-finite rows with a NaN scale.
-template <int G, int NV, int QMAX, bool PACK4, bool CHECK>
-__global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__ xin, int64_t rows, int K,
+// QMAX: 127 or 7; OUT: code layout; CHECK: flag non-finite rows with a NaN scale.
+// Row-major modes process `rows` rows.  Tiled modes process E * NB * 32 rows, where NB = ceil(N / 32) and
+// `rows` = E * N: launch row R is row n = R % (NB*32) of expert e = R / (NB*32); rows n >= N only write
+// zero codes (the padding of the last row block).
+template <int G, int NV, int QMAX, Out OUT, bool CHECK>
+__global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__ xin, int64_t rows, int K, int N,
                                                         void* __restrict__ qout, float* __restrict__ sout,
                                                         float* __restrict__ rot_out) {
+    constexpr bool kTiled = (OUT == Out::kTiledI8 || OUT == Out::kTiledI4);
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // wave-uniform
+    const int64_t lrow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int64_t row = lrow;          // source row (and scale index)
+    int64_t expert = 0;
+    int n = 0;
+    bool pad = false;
+    if constexpr (kTiled) {
+        const int nbr = ((N + 31) >> 5) << 5;  // rows per expert incl. padding
+        expert = lrow / nbr;
+        n = (int)(lrow - expert * nbr);
+        if (expert * N >= rows) return;  // wave-uniform
+        pad = n >= N;
+        row = expert * N + n;
+    } else {
+        if (row >= rows) return;  // wave-uniform
+    }
     const int nvec = K >> 3;
 
     Vec8 x[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int i = lane + 64 * j;
-        if (i < nvec) {
+        if (i < nvec && !pad) {
             if constexpr (G > 0) {
                 const uint4 raw = *reinterpret_cast<const uint4*>(
                     static_cast<const uint16_t*>(xin) + row * (int64_t)K + 8 * i);
@@ -141,33 +174,43 @@ __global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__
 #pragma unroll
             for (int e = 0; e < 8; ++e) c[e] = quant_code<QMAX>(x[j].v[e], scale);
         }
-        if constexpr (PACK4) {
+        if constexpr (OUT == Out::kRowI4 || OUT == Out::kTiledI4) {
             uint32_t packed = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) packed |= (uint32_t)(c[e] & 0xf) << (4 * e);
-            *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(qout) + row * (int64_t)(K / 2) + 4 * i) = packed;
+            const int64_t off = (OUT == Out::kRowI4)
+                                    ? row * (int64_t)(K / 2) + 4 * i
+                                    : expert * (int64_t)(((N + 31) >> 5) << 5) * (K / 2) + tiled_offset<true>(n, 8 * i, K);
+            *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(qout) + off) = packed;
         } else {
             uint2 o;
             o.x = pack4_i8(c[0], c[1], c[2], c[3]);
             o.y = pack4_i8(c[4], c[5], c[6], c[7]);
-            *reinterpret_cast<uint2*>(static_cast<int8_t*>(qout) + row * (int64_t)K + 8 * i) = o;
+            const int64_t off = (OUT == Out::kRowI8)
+                                    ? row * (int64_t)K + 8 * i
+                                    : expert * (int64_t)(((N + 31) >> 5) << 5) * K + tiled_offset<false>(n, 8 * i, K);
+            *reinterpret_cast<uint2*>(static_cast<int8_t*>(qout) + off) = o;
         }
+        if (pad) continue;
         if (rot_out) {
             float4* r = reinterpret_cast<float4*>(rot_out + row * (int64_t)K + 8 * i);
             r[0] = make_float4(x[j].v[0], x[j].v[1], x[j].v[2], x[j].v[3]);
             r[1] = make_float4(x[j].v[4], x[j].v[5], x[j].v[6], x[j].v[7]);
         }
     }
-    if (lane == 0) sout[row] = scale;
+    if (lane == 0 && !pad) sout[row] = scale;
 }
 
-template <int G, int QMAX, bool PACK4, bool CHECK>
-hipError_t launch_nv(const void* x, int64_t rows, int K, void* q, float* s, float* rot, hipStream_t st) {
+// rows: source rows (E * N for weights); N: rows per expert (tiled modes only).
+template <int G, int QMAX, Out OUT, bool CHECK>
+hipError_t launch_nv(const void* x, int64_t rows, int K, int N, void* q, float* s, float* rot, hipStream_t st) {
     const int nv = (K / 8 + 63) / 64;
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-#define CRK_NV_CASE(N)                                                                                   \
-    if (nv <= N) {                                                                                       \
-        rotq_rows_kernel<G, N, QMAX, PACK4, CHECK><<<grid, block, 0, st>>>(x, rows, K, q, s, rot);       \
+    int64_t launch_rows = rows;
+    if (OUT == Out::kTiledI8 || OUT == Out::kTiledI4) launch_rows = rows / N * (((N + 31) >> 5) << 5);
+    const dim3 grid((unsigned)((launch_rows + 3) / 4)), block(256);
+#define CRK_NV_CASE(NVC)                                                                                 \
+    if (nv <= NVC) {                                                                                     \
+        rotq_rows_kernel<G, NVC, QMAX, OUT, CHECK><<<grid, block, 0, st>>>(x, rows, K, N, q, s, rot);    \
         return hipGetLastError();                                                                        \
     }
     CRK_NV_CASE(1)
@@ -187,26 +230,37 @@ hipError_t launch_nv(const void* x, int64_t rows, int K, void* q, float* s, floa
 hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
                            hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    if (group == 256) return launch_nv<256, 127, false, false>(x, rows, K, q, s, rot, st);
-    return launch_nv<64, 127, false, false>(x, rows, K, q, s, rot, st);
+    if (group == 256) return launch_nv<256, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
+    return launch_nv<64, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
 }
 
-hipError_t launch_rotq_weights(const uint16_t* w, int64_t rows, int K, int group, int bits, void* q, float* s,
-                               hipStream_t st) {
+hipError_t launch_rotq_weights(const uint16_t* w, int E, int N, int K, int group, int bits, bool tiled, void* q,
+                               float* s, hipStream_t st) {
+    const int64_t rows = (int64_t)E * N;
     if (rows == 0) return hipSuccess;
+#define CRK_W(G, QMAX, OUTM) return launch_nv<G, QMAX, OUTM, true>(w, rows, K, N, q, s, nullptr, st)
     if (bits == 8) {
-        if (group == 256) return launch_nv<256, 127, false, true>(w, rows, K, q, s, nullptr, st);
-        return launch_nv<64, 127, false, true>(w, rows, K, q, s, nullptr, st);
+        if (tiled) {
+            if (group == 256) CRK_W(256, 127, Out::kTiledI8);
+            CRK_W(64, 127, Out::kTiledI8);
+        }
+        if (group == 256) CRK_W(256, 127, Out::kRowI8);
+        CRK_W(64, 127, Out::kRowI8);
     }
-    if (group == 256) return launch_nv<256, 7, true, true>(w, rows, K, q, s, nullptr, st);
-    return launch_nv<64, 7, true, true>(w, rows, K, q, s, nullptr, st);
+    if (tiled) {
+        if (group == 256) CRK_W(256, 7, Out::kTiledI4);
+        CRK_W(64, 7, Out::kTiledI4);
+    }
+    if (group == 256) CRK_W(256, 7, Out::kRowI4);
+    CRK_W(64, 7, Out::kRowI4);
+#undef CRK_W
 }
 
 hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,
                                       hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    if (bits == 8) return launch_nv<0, 127, false, false>(r, rows, K, q, s, nullptr, st);
-    return launch_nv<0, 7, false, false>(r, rows, K, q, s, nullptr, st);
+    if (bits == 8) return launch_nv<0, 127, Out::kRowI8, false>(r, rows, K, 0, q, s, nullptr, st);
+    return launch_nv<0, 7, Out::kRowI8, false>(r, rows, K, 0, q, s, nullptr, st);
 }
 
 }  // namespace crk
