@@ -75,21 +75,24 @@ def cpu_cores() -> int:
     return min(n, int(omp)) if omp and omp.isdigit() else n
 
 
-def cpu_baseline(x, lg, w_gu, w_dn, s, n_experts: int):
+def cpu_baseline(x, lg, w_gu, w_dn, s, n_experts: int, min_seconds: float = 10.0):
     """Time the CPU oracle (as it stands) on a bounded sample: the same T-token layer restricted to its first
     n_experts experts (same per-expert work: C tokens each through gate/up, SwiGLU, rotate+quantise, down,
-    combine).  Weight conversion is not timed, as on the GPU."""
+    combine), repeated until about `min_seconds` of CPU time.  Weight conversion is not timed, as on the GPU."""
     import oracle
     q_gu, s_gu = oracle.quantize_weights(w_gu[:n_experts], s.g_gu)
     q_dn, s_dn = oracle.quantize_weights(w_dn[:n_experts], s.g_dn)
     lg_s = np.ascontiguousarray(lg[:, :n_experts])
-    t0 = time.perf_counter()
-    oracle.moe_forward(x, lg_s, s.C, q_gu, s_gu, s.g_gu, q_dn, s_dn, s.g_dn)
-    dt = time.perf_counter() - t0
-    ops = 6.0 * n_experts * s.C * s.I * s.d
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt < min_seconds and reps < 64):
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, lg_s, s.C, q_gu, s_gu, s.g_gu, q_dn, s_dn, s.g_dn)
+        dt += time.perf_counter() - t0
+        reps += 1
+    ops = 6.0 * n_experts * s.C * s.I * s.d * reps
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle",
             "sample": f"T={s.T} layer restricted to experts 0..{n_experts - 1} (each C={s.C} tokens, full per-expert "
-                      f"work), {ops / 1e9:.1f} GOP in {dt:.2f} s, scaled to TOPS"}
+                      f"work), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s, scaled to TOPS"}
 
 
 def main():

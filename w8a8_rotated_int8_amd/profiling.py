@@ -1,0 +1,114 @@
+"""rocprofv3 summaries for the committed profiles: per-kernel duration statistics and HBM traffic per launch.
+
+Used by hand after a profiled run of ``bench.py``; reads only rocprofv3's CSV output (``--output-format csv
+-o run``) and writes short text summaries.  Nothing here runs a kernel except ``copy_probe``, the plain
+device-to-device copy of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters.
+
+    python -m w8a8_rotated_int8_amd.profiling stats <run_dir> <out.txt> "<command>"
+    python -m w8a8_rotated_int8_amd.profiling copy <MiB> <iters>
+    python -m w8a8_rotated_int8_amd.profiling traffic <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir>
+        <copy_MiB> <kernel_substring> <out.txt> "<commands>"
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEMM_SRC = os.path.join(ROOT, "w8a8_rotated_int8_amd", "csrc", "gemm.hip")
+
+
+def _csv(run_dir: str, suffix: str):
+    path = os.path.join(run_dir, f"run_{suffix}.csv")
+    if not os.path.exists(path):
+        cands = [os.path.join(dp, f) for dp, _, fs in os.walk(run_dir) for f in fs if f.endswith(f"_{suffix}.csv")]
+        if not cands:
+            raise FileNotFoundError(f"no *_{suffix}.csv under {run_dir}")
+        path = sorted(cands)[0]
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def short_name(name: str) -> str:
+    name = name.replace("crk::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return name if len(name) <= 110 else name[:107] + "..."
+
+
+def stats_summary(run_dir: str, out_txt: str, command: str) -> None:
+    rows = _csv(run_dir, "kernel_stats")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"command: {command}", "source: rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
+             f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total%':>7}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}  {short_name(r['Name'])}")
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counter_per_dispatch(run_dir: str, counter: str, pattern: str, skip: int = 1):
+    """Mean value of `counter` over the dispatches whose kernel name contains `pattern` (the first `skip`
+    dispatches are dropped as warm-up)."""
+    rows = [r for r in _csv(run_dir, "counter_collection") if pattern in r["Kernel_Name"]
+            and r["Counter_Name"] == counter]
+    per = collections.defaultdict(float)
+    for r in rows:
+        per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    ids = sorted(per)
+    if len(ids) > skip:
+        ids = ids[skip:]
+    if not ids:
+        raise ValueError(f"no dispatch of a kernel matching {pattern!r} with counter {counter}")
+    return sum(per[i] for i in ids) / len(ids), len(ids)
+
+
+def copy_probe(mib: int, iters: int) -> None:
+    """Plain device-to-device copy of `mib` MiB, `iters` times (counter calibration)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy probe: {iters} copies of {mib} MiB", flush=True)
+
+
+def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, pattern, out_txt, command):
+    nbytes = copy_mib << 20
+    cf, _ = counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy", skip=1)
+    cw, _ = counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy", skip=1)
+    f_scale = nbytes / (cf * 1024.0)
+    w_scale = nbytes / (cw * 1024.0)
+    kf, nf = counter_per_dispatch(fetch_dir, "FETCH_SIZE", pattern)
+    kw, nw = counter_per_dispatch(write_dir, "WRITE_SIZE", pattern)
+    fetch_b = kf * 1024.0 * f_scale
+    write_b = kw * 1024.0 * w_scale
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    lines = [f"command: {command}",
+             f"kernel: dispatches whose name contains {pattern!r} ({nf} FETCH, {nw} WRITE dispatches after warm-up)",
+             f"gemm_source_sha256_16: {sha}",
+             f"copy calibration: {copy_mib} MiB device copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB",
+             f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}",
+             f"fetch_kib_raw: {kf:.1f}", f"write_kib_raw: {kw:.1f}",
+             f"fetch_bytes_per_launch: {fetch_b:.6g}", f"write_bytes_per_launch: {write_b:.6g}",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.6g}"]
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1] if len(sys.argv) > 1 else ""
+    if cmd == "stats":
+        stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif cmd == "copy":
+        copy_probe(int(sys.argv[2]), int(sys.argv[3]))
+    elif cmd == "traffic":
+        traffic_summary(*sys.argv[2:6], int(sys.argv[6]), sys.argv[7], sys.argv[8], sys.argv[9])
+    else:
+        sys.exit(__doc__)
