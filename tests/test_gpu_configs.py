@@ -1,0 +1,96 @@
+"""GPU parity at the benchmark sizes, in the launch configuration the benchmark times.
+
+Every configuration is checked in full against the oracle (the oracle finishes one T = 8192 layer in seconds on
+the host cores): converted weight codes and scales, token codes and scales, routing indices and weights, the
+gate/up + SwiGLU rows, the hidden-row codes, the down rows and the combined output.  Each stage is also run on
+its own from the oracle's inputs, so a mismatch names the stage.  Bar: bit-exact for codes, scales and routing;
+BF16 within 1e-2 relative (and, the arithmetic being fully specified, expected bit-identical).
+
+  * T = 2048, C = 64 and T = 8192, C = 256 layers (64 experts, d = 2048, I = 1536), host-generated inputs;
+  * the 29-layer stack: layers 0 and 28 with 8-bit weights and layer 0 with 4-bit weights (weights drawn on the
+    GPU by torch's generator, copied to the host for the oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w8a8_rotated_int8_amd import binding as cr
+from w8a8_rotated_int8_amd import synth
+
+from helpers import DEV, assert_bf16_within, dev, dev_bf16, host, host_bf16, say, untile_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cr.lib()
+    oracle.load()
+
+
+def _check_layer(x, lg, w_gu_d, w_dn_d, w_gu, w_dn, shape, bits, what):
+    """x, lg, w_gu, w_dn: host arrays (bf16 bits / fp32); w_gu_d, w_dn_d: the same weights on the GPU."""
+    s = shape
+    say(f"{what}: converting weights (bits={bits})")
+    w = cr.quantize_moe_weights(w_gu_d, w_dn_d, s.g_gu, s.g_dn, bits)
+    q_gu, s_gu = oracle.quantize_weights(w_gu, s.g_gu, bits)
+    q_dn, s_dn = oracle.quantize_weights(w_dn, s.g_dn, bits)
+    cg = q_gu if bits == 8 else oracle.unpack_int4(q_gu, s.d)
+    cd = q_dn if bits == 8 else oracle.unpack_int4(q_dn, s.I)
+    assert np.array_equal(untile_codes(host(w.q_gu), s.E, 2 * s.I, s.d, bits), cg), "gate/up weight codes"
+    assert np.array_equal(untile_codes(host(w.q_dn), s.E, s.d, s.I, bits), cd), "down weight codes"
+    assert np.array_equal(host(w.s_gu).view(np.uint32), s_gu.view(np.uint32)), "gate/up weight scales"
+    assert np.array_equal(host(w.s_dn).view(np.uint32), s_dn.view(np.uint32)), "down weight scales"
+    del cg, cd
+
+    say(f"{what}: oracle layer")
+    ref = oracle.moe_forward(x, lg, s.C, q_gu, s_gu, s.g_gu, q_dn, s_dn, s.g_dn, bits, intermediates=True)
+
+    say(f"{what}: GPU layer")
+    xd, lgd = dev_bf16(x), dev(lg)
+    out, idx, wt = cr.moe_expert_choice_forward(xd, lgd, s.C, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), ref["idx"]), "routing indices"
+    assert np.array_equal(host(wt).view(np.uint32), ref["wt"].view(np.uint32)), "routing weights"
+    exact = assert_bf16_within(host_bf16(out), ref["out"], what=f"{what} out")
+    say(f"{what}: layer output {exact * 100:.3f}% bit-identical")
+    assert exact == 1.0
+
+    say(f"{what}: stages from the oracle's inputs")
+    qx, sx, _ = cr.convrot_rotq_rows(xd, s.g_gu)
+    assert np.array_equal(host(qx), ref["qx"]) and np.array_equal(host(sx).view(np.uint32),
+                                                                   ref["sx"].view(np.uint32)), "token codes"
+    idx_d = dev(ref["idx"])
+    a = cr.moe_gateup_swiglu(dev(ref["qx"]), dev(ref["sx"]), idx_d, w)
+    assert np.array_equal(host_bf16(a), ref["a"]), "gate/up + SwiGLU rows"
+    qa, sa, _ = cr.convrot_rotq_rows(dev_bf16(ref["a"]), s.g_dn)
+    assert np.array_equal(host(qa), ref["qa"]) and np.array_equal(host(sa).view(np.uint32),
+                                                                   ref["sa"].view(np.uint32)), "hidden codes"
+    z = cr.moe_down_proj(dev(ref["qa"]), dev(ref["sa"]), s.C, w)
+    assert np.array_equal(host_bf16(z), ref["z"]), "down rows"
+    o2 = cr.moe_combine(dev_bf16(ref["z"]), idx_d, dev(ref["wt"]), s.T)
+    assert np.array_equal(host_bf16(o2), ref["out"]), "combine"
+
+
+@pytest.mark.parametrize("cfg,bits", [(2, 8), (3, 8), (3, 4)])
+def test_full_size_layer(cfg, bits):
+    s = synth.CONFIGS[cfg]
+    what = f"config {cfg} T={s.T} C={s.C} bits={bits}"
+    say(f"{what}: generating inputs")
+    x, lg, w_gu, w_dn = synth.moe_inputs(cfg)
+    _check_layer(x, lg, dev_bf16(w_gu), dev_bf16(w_dn), w_gu, w_dn, s, bits, what)
+
+
+@pytest.mark.parametrize("layer,bits", [(0, 8), (28, 8), (0, 4)])
+def test_layer_stack(layer, bits):
+    s = synth.CONFIGS[4]
+    what = f"stack layer {layer} bits={bits}"
+    say(f"{what}: drawing weights on the GPU")
+    lgd, w_gu_d, w_dn_d = synth.stack_layer_device(layer, s, DEV)
+    x = synth.stack_x(s)
+    lg = host(lgd)
+    w_gu = host_bf16(w_gu_d)
+    w_dn = host_bf16(w_dn_d)
+    _check_layer(x, lg, w_gu_d, w_dn_d, w_gu, w_dn, s, bits, what)

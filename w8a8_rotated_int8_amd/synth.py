@@ -113,6 +113,11 @@ def moe_inputs(cfg: int, shape: MoEShape | None = None, seed_base: int | None = 
     return x, lg, w_gu, w_dn
 
 
+def stack_x(shape: MoEShape) -> np.ndarray:
+    """The tokens every layer of the 29-layer stack takes (host bf16 bits [T, d]; seed base 4000)."""
+    return activations(4000, shape.T, shape.d)
+
+
 def stack_layer_device(layer: int, shape: MoEShape, device):
     """One layer of the 29-layer stack drawn on the GPU: (logits fp32, W_gu bf16, W_dn bf16) torch tensors."""
     import torch
