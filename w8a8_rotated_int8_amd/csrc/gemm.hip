@@ -8,22 +8,34 @@
 // dequantise on the fly as on the XB_UNetLoaderINTROCm page), inside the expert-choice MoE of
 // "MLX Nucleus-Image" (SwiGLU convention silu(gate) * up, gate = first half of the fused projection).
 //
-// Work decomposition.  One workgroup (4 wavefronts) per (expert e, N-tile of 256 output columns, M-block of
-// BM <= 128 rows); two workgroups share a CU.  The M-blocks of one (expert, N-tile) are consecutive tiles, so
-// the weight panel is streamed from HBM once and re-read from L2 by the other M-blocks.  Wavefront w owns all BM rows and two 32-column blocks (for SwiGLU: the
-// gate block and the up block of the same 32 columns, so the epilogue pairs them in registers).  Workgroup
-// ids are remapped so that the N-tiles of one expert run on one XCD and share its L2 for the activations.
+// Work decomposition.  A tile is (expert e, N-tile of 256 weight rows, M-block of BM <= 256 rows).  For the
+// MoE one M-block holds all C <= 256 slots of an expert, so every weight byte is streamed from HBM exactly
+// once per layer.  The kernel is persistent: one workgroup of 8 wavefronts per CU (the LDS budget admits one)
+// walks a sequence of tiles.  The tiles are split into 8 contiguous ranges, one per XCD (workgroup g runs on
+// XCD g % 8), and the workgroups of an XCD take the tiles of its range round robin, so at any time they work
+// on neighbouring N-tiles of the same experts and share the gathered activation rows in that XCD's L2.
 //
-// Main loop, K-steps of 64 (two 32-deep MFMA slices), S-stage software pipeline:
-//   * activations (gathered token rows for gate/up, contiguous slot rows for down) go global -> LDS with
-//     gfx950's global_load_lds_dwordx4 into an S-deep LDS ring; rows are 64 bytes, 16-byte chunks XOR-
-//     swizzled by (row / 4) % 4 so the 16-byte fragment reads are bank-conflict free;
-//   * weights take the same DMA path into a wavefront-private LDS region of each stage: the MFMA-tiled
-//     layout makes every (32-row block, K-block) tile 1 KiB in B-operand lane order, so each DMA is one
-//     coalesced 16-byte load per lane and the fragment read is a contiguous ds_read_b128;
-//   * per K-step: wait for the oldest stage (explicit vmcnt; every load of the loop is a DMA, so the count
-//     is exact and no register load stalls the MFMAs), one workgroup barrier, issue the loads of stage
-//     kt+S-1, then TM x 2 x 2 MFMAs on stage kt.
+// Wavefront w computes rows [(w / 4) * BM/2, +BM/2) of the tile against two 32-row weight blocks picked by
+// w % 4 (for SwiGLU the gate block and the up block of the same 32 output columns, so the epilogue pairs
+// them in registers).
+//
+// Main loop: K-steps of 64 bytes (two 32-deep MFMA slices), one pipeline running across all tiles of the
+// workgroup, so the loads of the next tile's first stages overlap the current tile's last steps and its
+// epilogue.
+//   * Every operand moves global -> LDS with gfx950's global_load_lds (no register staging): the weights, the
+//     gathered activation rows, the per-tile row indices, row scales and column scales.
+//   * Weights are stored MFMA-tiled: each (32-row block, K-block) tile is 1 KiB in B-operand lane order, so a
+//     DMA is one coalesced 16-byte load per lane (non-temporal: each byte is used once) and the fragment read
+//     is one ds_read_b128.  Activation rows are 64 bytes per stage with the 16-byte chunks XOR-swizzled by
+//     (row / 4) % 4, so the fragment reads are free of bank conflicts.
+//   * Load roles: wavefronts 0-3 issue the weight DMAs into an SB-deep ring, wavefronts 4-7 the activation
+//     DMAs into an SA-deep ring.  A wavefront's vector memory operations complete in issue order, so waiting
+//     for vmcnt <= X, where X counts operations it issued after a stage, proves that the stage has landed.
+//     Every wavefront counts the operations it issues (DMAs, and the epilogue's buffer stores, which are
+//     always issued and drop out-of-range lanes in hardware) and waits with that exact X: the weight ring
+//     stays SB-1 stages ahead through tile boundaries and epilogues, the activation ring SA-1.  Operations
+//     left out of the count can only make a wait stricter.  One workgroup barrier per K-step publishes both
+//     rings.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
 #include "device_common.h"
@@ -36,11 +48,14 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBK = 64;    // K bytes per pipeline stage (two MFMA slices)
-constexpr int kBN = 256;   // output columns per workgroup (4 wavefronts x 2 blocks of 32)
-constexpr int kThreads = 256;
-// Cache policy of the weight DMAs: non-temporal (each weight byte is used by one workgroup, or by the M-blocks
-// of one N-tile right after each other); streaming with nt measured ~6.5 TB/s vs ~5.7 TB/s without.
+constexpr int kBK = 64;          // K bytes per pipeline stage (two MFMA slices)
+constexpr int kBN = 256;         // weight rows per tile (8 blocks of 32)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStgBytes = 2048;           // per wavefront: one 32 x 32 bf16 block of the epilogue
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw (untyped) gfx9 buffer access
+constexpr int kOobOffset = 0x40000000;    // byte offset past every output range (the store is dropped)
+// Cache policy of the weight DMAs: non-temporal; streaming with nt measured ~6.5 TB/s vs ~5.7 TB/s without.
 constexpr int kNonTemporal = 2;
 
 // Sign-extend the 8 nibbles of w (code 2j in the low nibble of byte j) into 8 int8 bytes, in k order.
@@ -55,8 +70,8 @@ __device__ __forceinline__ uint2 unpack_nibbles(uint32_t w) {
     return r;
 }
 
-// LDS byte offset of 16-byte chunk c (0..3) of row r inside one activation stage.
-__device__ __forceinline__ int a_lds_offset(int r, int c) { return r * kBK + ((c ^ ((r >> 2) & 3)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..3) of 64-byte row r: activation stages and epilogue staging blocks.
+__device__ __forceinline__ int swz_offset(int r, int c) { return r * kBK + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] in bits 15:14).
@@ -65,152 +80,273 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// OCC: wavefronts per SIMD the register budget must allow (2: two workgroups share a CU, so one workgroup's
-// epilogue overlaps the other's MFMA loop).
-template <int BM, int S, int OCC, Epi EPI, int WBITS, bool TILED>
-__global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_kernel(const GemmProblem p, int tiles_m, int tiles_n) {
-    constexpr int TM = BM / 32;                 // 32-row blocks per wavefront
-    constexpr int NA = BM / 64;                 // activation DMA instructions per thread per stage
-    constexpr int NBT = (WBITS == 8) ? 4 : 2;   // 1 KiB weight tiles per wavefront per stage
-    constexpr int A_BYTES = BM * kBK;
-    constexpr int B_WAVE = NBT * 1024;
-    constexpr int STAGE = A_BYTES + 4 * B_WAVE;
-    static_assert(BM % 64 == 0 && S >= 2, "tile config");
+// vmcnt(x) for a wave-uniform x (binary search over the immediate forms; scalar branches only).
+template <int L, int H>
+__device__ __forceinline__ void wait_vmcnt_range(int x) {
+    if constexpr (L == H) {
+        wait_vmcnt<L>();
+    } else {
+        constexpr int Mid = (L + H) / 2;
+        if (x <= Mid)
+            wait_vmcnt_range<L, Mid>(x);
+        else
+            wait_vmcnt_range<Mid + 1, H>(x);
+    }
+}
+__device__ __forceinline__ void wait_vmcnt_dyn(int x) {
+    x = x < 0 ? 0 : (x > 63 ? 63 : x);  // a smaller count is a stricter wait
+    wait_vmcnt_range<0, 63>(x);
+}
+
+template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
+struct GemmCfg {
+    static constexpr int TM = BM / 64;                 // 32-row blocks per wavefront (BM/2 rows)
+    static constexpr int NBT = (WBITS == 8) ? 16 : 8;  // 1 KiB weight tiles per stage
+    static constexpr int NBW = NBT / 4;                // weight DMAs per loader wavefront per stage
+    static constexpr int A_BYTES = BM * kBK;
+    static constexpr int NAW = A_BYTES / 4096;         // activation DMAs per loader wavefront per stage
+    static constexpr int B_BYTES = NBT * 1024;
+    static constexpr int B_RING = SB * B_BYTES;
+    static constexpr int A_RING = SA * A_BYTES;
+    static constexpr bool STG_IN_RING = B_BYTES >= kWaves * kStgBytes;  // staging in the consumed weight slot
+    static constexpr int CSC_OFF = B_RING + A_RING;          // SB slots of 256 column scales
+    static constexpr int SROW_OFF = CSC_OFF + SB * kBN * 4;  // SA slots of BM row scales
+    static constexpr int ROWS_OFF = SROW_OFF + SA * BM * 4;  // 2 slots of BM gathered row indices
+    static constexpr int STG_OFF = ROWS_OFF + 2 * BM * 4;
+    static constexpr int LDS = STG_OFF + (STG_IN_RING ? 0 : kWaves * kStgBytes);
+    static constexpr int SMAX = SB > SA ? SB : SA;
+    static_assert(BM == 64 || BM == 128 || BM == 256, "tile rows");
+    static_assert(NAW >= 1 && NAW * 4096 == A_BYTES, "activation stage / loader mismatch");
+    static_assert(SB >= 2 && SA >= 3, "ring depth");
     static_assert(TILED || WBITS == 8, "4-bit weights are only stored tiled");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
 
-    // LDS: S stages of [activations | weights] (reused to stage the output tile after the main loop), then
-    // the BM activation-row scales.
+template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmProblem p, int tiles_m, int tiles_n) {
+    using Cfg = GemmCfg<BM, SB, SA, EPI, WBITS, TILED>;
+    constexpr int TM = Cfg::TM, NBW = Cfg::NBW, NAW = Cfg::NAW;
+    constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
+    constexpr int HALF = BM / 2;
+    constexpr bool kScales = EPI != Epi::kI32;
+
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-    constexpr int OUT_COLS = (EPI == Epi::kSwiGLU) ? kBN / 2 : kBN;
-    constexpr int OUT_STRIDE = OUT_COLS * 2 + 16;  // bytes per staged output row (padded against bank conflicts)
-    constexpr int RING = (S * STAGE > BM * OUT_STRIDE) ? S * STAGE : BM * OUT_STRIDE;
-    float* srow_lds = reinterpret_cast<float*>(smem + RING);
-
-    const int total = p.E * tiles_m * tiles_n;
-    const int tile = xcd_remap((int)blockIdx.x, total);
-    // M-blocks fastest: the M-blocks of one N-tile stream the same weight panel back to back on one XCD, so
-    // all but the first read it from L2.
-    const int mt = tile % tiles_m;
-    const int nt = (tile / tiles_m) % tiles_n;
-    const int e = tile / (tiles_n * tiles_m);
+    int8_t* const b_ring = smem;
+    int8_t* const a_ring = smem + Cfg::B_RING;
+    float* const csc_lds = reinterpret_cast<float*>(smem + Cfg::CSC_OFF);
+    float* const srow_lds = reinterpret_cast<float*>(smem + Cfg::SROW_OFF);
+    int32_t* const rows_lds = reinterpret_cast<int32_t*>(smem + Cfg::ROWS_OFF);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches stay scalar
+    const int mh = wave >> 2;  // M-half computed by this wavefront
+    const int nq = wave & 3;   // weight-block pair computed by this wavefront; DMA share of the weight loaders
+    const bool b_loader = wave < 4;
+    const int aw = wave - 4;   // activation loader index (0..3)
     const int M = p.M, N = p.N, K = p.K;
     const int I = N >> 1;
     const int nk = (K + kBK - 1) / kBK;
+    const int NBk = (N + 31) >> 5;  // row blocks per expert
+    // Gathered row indices reach the activation loaders through LDS when the index DMA of tile i+1, issued
+    // with the first stage of tile i, is published by the time tile i+1's loads are issued (nk >= SA - 1).
+    const bool rows_via_lds = p.a_rows != nullptr && nk >= SA - 1;
 
-    // ---- activation sources: DMA instruction j of this wavefront fills LDS chunk slot s = (4j + w)*64 + lane ----
-    const int8_t* a_src[NA];
-    int a_koff[NA];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-        const int slot = (4 * j + wave) * 64 + lane;
-        const int r = slot >> 2;                     // tile row
-        const int c = (slot & 3) ^ ((r >> 2) & 3);   // logical 16-byte chunk held by that slot
+    // ---- this workgroup's tiles: XCD x owns the contiguous range [xs, xs + xn); its workgroups interleave ----
+    const int total = p.E * tiles_m * tiles_n;
+    const int G = (int)gridDim.x;
+    const int xcd = (int)blockIdx.x % 8, local = (int)blockIdx.x / 8;
+    const int nwg_x = (G - xcd + 7) / 8;
+    const int base = total / 8, extra = total % 8;
+    const int xs = xcd * base + (xcd < extra ? xcd : extra);
+    const int xn = base + (xcd < extra ? 1 : 0);
+    const int my_tiles = local < xn ? (xn - local + nwg_x - 1) / nwg_x : 0;
+    if (my_tiles == 0) return;  // workgroup-uniform
+    const int total_stages = my_tiles * nk;
+    // M-blocks fastest, then N-tiles, then experts
+    auto decode = [&](int i, int& e, int& nt, int& mt) {
+        const int t = xs + local + i * nwg_x;
+        mt = t % tiles_m;
+        nt = (t / tiles_m) % tiles_n;
+        e = t / (tiles_m * tiles_n);
+    };
+    // weight row block held by stage block j (0..7) of N-tile nt; SwiGLU: blocks 0..3 are the gate blocks of
+    // the tile's 4 output column blocks, blocks 4..7 their up blocks
+    auto wblk = [&](int j, int nt) -> int {
+        if constexpr (EPI == Epi::kSwiGLU) {
+            const int jb = nt * 4 + (j & 3);
+            return j < 4 ? jb : (I >> 5) + jb;
+        } else {
+            return nt * 8 + j;
+        }
+    };
+    const int my_blk0 = (EPI == Epi::kSwiGLU) ? nq : 2 * nq;
+    const int my_blk1 = (EPI == Epi::kSwiGLU) ? nq + 4 : 2 * nq + 1;
+    auto slot_index = [&](int e, int mt, int r) -> int64_t {
         int m = mt * BM + r;
         m = m < M ? m : M - 1;
-        const int64_t sl = (int64_t)e * M + m;
-        int64_t arow = p.a_rows ? (int64_t)p.a_rows[sl] : sl;
-        arow = arow < 0 ? 0 : (arow < p.a_nrows ? arow : p.a_nrows - 1);
-        a_src[j] = p.A + arow * K;
-        a_koff[j] = c * 16;
-    }
+        return (int64_t)e * M + m;
+    };
+    auto clamp_row = [&](int64_t arow) -> int64_t {
+        return arow < 0 ? 0 : (arow < p.a_nrows ? arow : p.a_nrows - 1);
+    };
 
-    // ---- weight blocks of this wavefront: q = 0, 1 ----
-    int nblk[2];
-    if constexpr (EPI == Epi::kSwiGLU) {
-        const int jb = nt * 4 + wave;             // 32-column block of the gate/up halves
-        nblk[0] = jb;                             // gate rows jb*32 ..
-        nblk[1] = (I >> 5) + jb;                  // up rows I + jb*32 ..
-    } else {
-        nblk[0] = nt * 8 + 2 * wave;
-        nblk[1] = nt * 8 + 2 * wave + 1;
-    }
-    const int NBk = (N + 31) >> 5;                // row blocks per expert
-    const int8_t* b_base[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int nb = nblk[q] < NBk ? nblk[q] : NBk - 1;  // out-of-range blocks compute unused columns
-        if constexpr (TILED) {
-            const int64_t expert_bytes = (int64_t)NBk * 32 * K * WBITS / 8;
-            b_base[q] = static_cast<const int8_t*>(p.B) + e * expert_bytes + (int64_t)nb * 32 * K * WBITS / 8 +
-                        lane * 16;
-        } else {
-            int n = nb * 32 + (lane & 31);
-            n = n < N ? n : N - 1;
-            b_base[q] = static_cast<const int8_t*>(p.B) + ((int64_t)e * N + n) * K + (lane >> 5) * 16;
-        }
-    }
+    // ---- count of vector memory operations this wavefront issued, and the count after each pending stage ----
+    int ops = 0;
+    int hist[Cfg::SMAX];
+    const int S = b_loader ? SB : SA;  // this wavefront's ring depth
 
-    // Loads of one stage.  Tiled weights: every 1 KiB tile is DMA'd into this wavefront's private LDS region
-    // in lane order (exactly the MFMA operand layout).  Row-major weights (test path): registers with zero
-    // fill past K, then ds_write into the same place.
-    auto issue = [&](int kt, int buf) {
-        int8_t* st = smem + buf * STAGE;
-        const int k0 = kt * kBK;
+    // ---- loader state for the tile whose stages are being issued ----
+    // weight loaders: DMA j covers stage tile t = nq * NBW + j: (block, slice) = (t / 2, t % 2) for int8,
+    // block t for int4 (both slices in one tile)
+    // activation loaders: DMA j fills LDS chunk slot s = (4 j + aw) * 64 + lane
+    constexpr int NLMAX = NBW > NAW ? NBW : NAW;
+    const int8_t* src[NLMAX];
+    int src_off[NLMAX];
+    int ld_tile = -1;
+    auto set_loader_tile = [&](int i) {
+        int e, nt, mt;
+        decode(i, e, nt, mt);
+        if (b_loader) {
 #pragma unroll
-        for (int j = 0; j < NA; ++j) {
-            int k = k0 + a_koff[j];
-            k = k <= K - 16 ? k : K - 16;  // past K the weights are zero, any in-bounds bytes do
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(a_src[j] + k),
-                                             (lds_void*)(st + (4 * j + wave) * 1024), 16, 0, 0);
-        }
-        int8_t* bw = st + A_BYTES + wave * B_WAVE;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            if constexpr (TILED && WBITS == 8) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    __builtin_amdgcn_global_load_lds(static_cast<const void*>(b_base[q] + (int64_t)(2 * kt + s) * 1024),
-                                                     (lds_void*)(bw + (2 * q + s) * 1024), 16, 0, kNonTemporal);
-            } else if constexpr (TILED) {
-                __builtin_amdgcn_global_load_lds(static_cast<const void*>(b_base[q] + (int64_t)kt * 1024),
-                                                 (lds_void*)(bw + q * 1024), 16, 0, kNonTemporal);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int k = k0 + s * 32 + (lane >> 5) * 16;
-                    const v4i v = (k + 16 <= K) ? *reinterpret_cast<const v4i*>(b_base[q] + k0 + s * 32)
-                                                : v4i{0, 0, 0, 0};
-                    *reinterpret_cast<v4i*>(bw + (2 * q + s) * 1024 + lane * 16) = v;
+            for (int j = 0; j < NLMAX; ++j) {
+                src[j] = p.A;
+                src_off[j] = 0;
+                if (j >= NBW) continue;
+                const int t = nq * NBW + j;
+                const int blk = (WBITS == 8) ? t / 2 : t;
+                int nb = wblk(blk, nt);
+                nb = nb < NBk ? nb : NBk - 1;  // out-of-range blocks compute unused columns
+                if constexpr (TILED) {
+                    const int64_t expert_bytes = (int64_t)NBk * 32 * K * WBITS / 8;
+                    src[j] = static_cast<const int8_t*>(p.B) + e * expert_bytes + (int64_t)nb * 32 * K * WBITS / 8 +
+                             lane * 16 + ((WBITS == 8) ? (t & 1) * 1024 : 0);
+                } else {
+                    int n = nb * 32 + (lane & 31);
+                    n = n < N ? n : N - 1;
+                    src[j] = static_cast<const int8_t*>(p.B) + ((int64_t)e * N + n) * K + (lane >> 5) * 16;
+                    src_off[j] = (t & 1) * 32;  // slice
                 }
+            }
+            if constexpr (kScales) {
+                // column scales of the tile; lane l of weight loader w fetches column (2w + l / 32) * 32 + l % 32
+                const int j = 2 * nq + (lane >> 5);
+                int n = wblk(j, nt) * 32 + (lane & 31);
+                n = n < N ? n : N - 1;
+                __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.b_scale + (int64_t)e * N + n),
+                                                 (lds_void*)(csc_lds + (i % SB) * kBN + nq * 64), 4, 0, 0);
+                ++ops;
+            }
+        } else {
+            const int32_t* rows_cur = rows_lds + (i & 1) * BM;
+            auto arow_of = [&](int r) -> int64_t {
+                if (p.a_rows == nullptr) return slot_index(e, mt, r);
+                if (rows_via_lds && i > 0) return clamp_row(rows_cur[r]);
+                return clamp_row(p.a_rows[slot_index(e, mt, r)]);  // first tile, or K too short to prefetch
+            };
+#pragma unroll
+            for (int j = 0; j < NLMAX; ++j) {
+                src[j] = p.A;
+                src_off[j] = 0;
+                if (j >= NAW) continue;
+                const int slot = (4 * j + aw) * 64 + lane;
+                const int r = slot >> 2;                    // tile row
+                const int c = (slot & 3) ^ ((r >> 2) & 3);  // logical 16-byte chunk held by that slot
+                src[j] = p.A + arow_of(r) * K;
+                src_off[j] = c * 16;
+            }
+            if (aw * 64 < BM) {
+                const int r = aw * 64 + lane;
+                if constexpr (kScales) {
+                    __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.a_scale + arow_of(r)),
+                                                     (lds_void*)(srow_lds + (i % SA) * BM + aw * 64), 4, 0, 0);
+                    ++ops;
+                }
+                if (rows_via_lds && i + 1 < my_tiles) {
+                    // raw row indices of the next tile (clamped where they are read)
+                    int e1, nt1, mt1;
+                    decode(i + 1, e1, nt1, mt1);
+                    __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.a_rows + slot_index(e1, mt1, r)),
+                                                     (lds_void*)(rows_lds + ((i + 1) & 1) * BM + aw * 64), 4, 0, 0);
+                    ++ops;
+                }
+            }
+        }
+        ld_tile = i;
+    };
+
+    // Loads of global stage g (tile g / nk, K-step g % nk) into ring slot g % S of this wavefront's role.
+    auto issue = [&](int g) {
+        const int i = g / nk, kt = g - i * nk;
+        if (i != ld_tile) set_loader_tile(i);
+        if (b_loader) {
+            int8_t* st = b_ring + (g % SB) * B_BYTES;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const int t = nq * NBW + j;
+                if constexpr (TILED) {
+                    const int64_t off = (WBITS == 8) ? (int64_t)(2 * kt) * 1024 : (int64_t)kt * 1024;
+                    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[j] + off), (lds_void*)(st + t * 1024),
+                                                     16, 0, kNonTemporal);
+                    ++ops;
+                } else {
+                    // row-major weights (plain GEMM) go through registers, zero past K; not counted: the
+                    // ds_write is waited for (lgkmcnt) before the barrier that publishes the stage
+                    const int k = kt * kBK + src_off[j] + (lane >> 5) * 16;
+                    const v4i v = (k + 16 <= K) ? *reinterpret_cast<const v4i*>(src[j] + kt * kBK + src_off[j])
+                                                : v4i{0, 0, 0, 0};
+                    *reinterpret_cast<v4i*>(st + t * 1024 + lane * 16) = v;
+                }
+            }
+        } else {
+            int8_t* st = a_ring + (g % SA) * A_BYTES;
+#pragma unroll
+            for (int j = 0; j < NAW; ++j) {
+                int k = kt * kBK + src_off[j];
+                k = k <= K - 16 ? k : K - 16;  // past K the weights are zero, any in-bounds bytes do
+                __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[j] + k),
+                                                 (lds_void*)(st + (4 * j + aw) * 1024), 16, 0, 0);
+                ++ops;
             }
         }
     };
 
     v16i acc[TM][2];
+    auto clear_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][q][r] = 0;
+                for (int r = 0; r < 16; ++r) acc[i][q][r] = 0;
+    };
 
-    // All fragments of both slices are read first (20 ds_read_b128 for BM = 256), so the LDS latency of later
-    // fragments hides under the MFMAs of earlier ones.
-    auto compute = [&](int buf) {
-        const int8_t* As = smem + buf * STAGE;
-        const int8_t* bw = As + A_BYTES + wave * B_WAVE + lane * 16;
+    // All fragments of both slices are read first, so the LDS latency of later fragments hides under the
+    // MFMAs of earlier ones.
+    auto compute = [&](int g) {
+        const int8_t* As = a_ring + (g % SA) * A_BYTES;
+        const int8_t* Bs = b_ring + (g % SB) * B_BYTES + lane * 16;
         v4i bf[2][2];
         v4i af[2][TM];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
+                const int blk = q ? my_blk1 : my_blk0;
                 if constexpr (WBITS == 8) {
-                    bf[s][q] = *reinterpret_cast<const v4i*>(bw + (2 * q + s) * 1024);
+                    bf[s][q] = *reinterpret_cast<const v4i*>(Bs + (2 * blk + s) * 1024);
                 } else {
-                    const uint2 w = *reinterpret_cast<const uint2*>(bw + q * 1024 + 8 * s);
+                    const uint2 w = *reinterpret_cast<const uint2*>(Bs + blk * 1024 + 8 * s);
                     const uint2 u0 = unpack_nibbles(w.x), u1 = unpack_nibbles(w.y);
                     bf[s][q] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
                 }
             }
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
-                af[s][tm] = *reinterpret_cast<const v4i*>(As + a_lds_offset(tm * 32 + (lane & 31), 2 * s + (lane >> 5)));
+                af[s][tm] = *reinterpret_cast<const v4i*>(
+                    As + swz_offset(mh * HALF + tm * 32 + (lane & 31), 2 * s + (lane >> 5)));
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -219,164 +355,193 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_kernel(const GemmP
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
                     acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s][tm], bf[s][q], acc[tm][q], 0, 0, 0);
-        // Scheduling order: every LDS read of the stage, then the MFMAs (the waitcnt pass then waits only for
-        // the fragments each MFMA needs).
+        // Scheduling order: every LDS read of the stage, then the MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + 2), 0);  // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * TM, 0);        // MFMAs
     };
 
-    // Row scales of the tile (gathered like the activation rows) into LDS, column scales into registers;
-    // issued before the pipeline so their latency hides under it.
-    float csc[2] = {0.0f, 0.0f};
-    if constexpr (EPI != Epi::kI32) {
-        for (int r = tid; r < BM; r += kThreads) {
-            int m = mt * BM + r;
-            m = m < M ? m : M - 1;
-            const int64_t sl = (int64_t)e * M + m;
-            int64_t arow = p.a_rows ? (int64_t)p.a_rows[sl] : sl;
-            arow = arow < 0 ? 0 : (arow < p.a_nrows ? arow : p.a_nrows - 1);
-            srow_lds[r] = p.a_scale[arow];
-        }
+    // Epilogue of tile i, run at global stage g (its last).  Lane l holds column l % 32 and rows
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of each 32 x 32 accumulator block.
+    auto epilogue = [&](int i, int g) {
+        int e, nt, mt;
+        decode(i, e, nt, mt);
+        const int col = lane & 31;
+        if constexpr (EPI == Epi::kI32) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            int n = nblk[q] * 32 + (lane & 31);
-            n = n < N ? n : N - 1;
-            csc[q] = p.b_scale[(int64_t)e * N + n];
-        }
-    }
-
-    // prologue: stages 0 .. S-2 in flight
-    for (int u = 0; u < S - 1 && u < nk; ++u) issue(u, u);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        // Every stage is NA + NBT DMA instructions per thread (in issue order); stages kt+1 .. kt+S-2 may
-        // still be in flight.
-        if (kt + S - 2 < nk)
-            wait_vmcnt<(S - 2) * (NA + NBT)>();
-        else
-            wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // all stage-kt data landed; everyone is done with stage kt-1
-        // keeps the LDS reads of stage kt below the barrier (costs an lgkmcnt wait, not a vmcnt one)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-        compute(kt % S);
-    }
-
-    // ---- epilogue: lane holds column (lane & 31) and rows 8(r/4) + 4(lane/32) + r%4 of each 32x32 block ----
-    const int col = lane & 31;
-    if constexpr (EPI == Epi::kI32) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int mbase = mt * BM + tm * 32 + (lane >> 5) * 4;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int n = nblk[q] * 32 + col;
-                if (n >= N) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = mbase + (r >> 2) * 8 + (r & 3);
-                    if (m < M) static_cast<int32_t*>(p.out)[((int64_t)e * M + m) * N + n] = acc[tm][q][r];
-                }
-            }
-        }
-        return;
-    } else {
-        // bf16 results go to an LDS copy of the output tile, then out with coalesced 16-byte stores.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // every wavefront is done with the ring
-        int8_t* stage = smem;
-        float bias[2] = {0.0f, 0.0f};
-        if constexpr (EPI == Epi::kBf16) {
-            if (p.bias) {
+            for (int tm = 0; tm < TM; ++tm) {
+                const int mbase = mt * BM + mh * HALF + tm * 32 + (lane >> 5) * 4;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    int n = nblk[q] * 32 + col;
-                    n = n < N ? n : N - 1;
-                    bias[q] = bf16_to_float(p.bias[n]);
-                }
-            }
-        }
+                    const int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + col;
+                    if (n >= N) continue;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int lr = tm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row within the tile
-                const float sr = srow_lds[lr];
-                if constexpr (EPI == Epi::kBf16) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        float v = (float)acc[tm][q][r];
-                        v = v * sr;
-                        v = v * csc[q];
-                        if (p.bias) v = v + bias[q];
-                        const int lc = (2 * wave + q) * 32 + col;  // column within the tile
-                        *reinterpret_cast<uint16_t*>(stage + lr * OUT_STRIDE + lc * 2) = (uint16_t)float_to_bf16(v);
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = mbase + (r >> 2) * 8 + (r & 3);
+                        if (m < M) static_cast<int32_t*>(p.out)[((int64_t)e * M + m) * N + n] = acc[tm][q][r];
                     }
-                } else {
-                    float g = (float)acc[tm][0][r];
-                    g = g * sr;
-                    g = g * csc[0];
-                    float u = (float)acc[tm][1][r];
-                    u = u * sr;
-                    u = u * csc[1];
-                    const float gb = bf16_to_float(float_to_bf16(g));
-                    const float ub = bf16_to_float(float_to_bf16(u));
-                    const float a = silu_fixed(gb) * ub;
-                    const int lc = wave * 32 + col;
-                    *reinterpret_cast<uint16_t*>(stage + lr * OUT_STRIDE + lc * 2) = (uint16_t)float_to_bf16(a);
                 }
-            }
-        }
-        __syncthreads();
-        const int ldo = (EPI == Epi::kSwiGLU) ? I : N;                  // output row length (elements)
-        const int col0 = (EPI == Epi::kSwiGLU) ? nt * (kBN / 2) : nt * kBN;
-        const int ncols = (ldo - col0) < OUT_COLS ? (ldo - col0) : OUT_COLS;
-        constexpr int CPR = OUT_COLS / 8;                                // 16-byte chunks per tile row
-        uint16_t* out = static_cast<uint16_t*>(p.out);
-        if ((ldo & 7) == 0) {
-            for (int c = tid; c < BM * CPR; c += kThreads) {
-                const int lr = c / CPR, ch = c % CPR;
-                const int m = mt * BM + lr;
-                if (m >= M || ch * 8 >= ncols) continue;
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + lr * OUT_STRIDE + ch * 16);
-                *reinterpret_cast<uint4*>(out + ((int64_t)e * M + m) * ldo + col0 + ch * 8) = v;
             }
         } else {
-            for (int c = tid; c < BM * OUT_COLS; c += kThreads) {
-                const int lr = c / OUT_COLS, cc = c % OUT_COLS;
-                const int m = mt * BM + lr;
-                if (m >= M || cc >= ncols) continue;
-                out[((int64_t)e * M + m) * ldo + col0 + cc] =
-                    *reinterpret_cast<const uint16_t*>(stage + lr * OUT_STRIDE + cc * 2);
+            // every wavefront is done with stage g, so its weight slot can hold the staging blocks; the next
+            // loads into that slot are issued after the following K-step's barrier
+            __builtin_amdgcn_s_barrier();
+            int8_t* stg = (Cfg::STG_IN_RING ? b_ring + (g % SB) * B_BYTES : smem + Cfg::STG_OFF) + wave * kStgBytes;
+            const float* srow = srow_lds + (i % SA) * BM + mh * HALF;
+            const float* csc = csc_lds + (i % SB) * kBN;
+            float cs[2], bias[2] = {0.0f, 0.0f};
+            cs[0] = csc[my_blk0 * 32 + col];
+            cs[1] = csc[my_blk1 * 32 + col];
+            if constexpr (EPI == Epi::kBf16) {
+                if (p.bias) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + col;
+                        n = n < N ? n : N - 1;
+                        bias[q] = bf16_to_float(p.bias[n]);
+                    }
+                }
             }
+            const int ldo = (EPI == Epi::kSwiGLU) ? I : N;  // output row length (elements)
+            const int rows_valid = (M - mt * BM) < BM ? (M - mt * BM) : BM;
+            uint16_t* const obase = static_cast<uint16_t*>(p.out) + ((int64_t)e * M + mt * BM) * ldo;
+            const bool vec_store = (ldo & 7) == 0;
+            const __amdgpu_buffer_rsrc_t orsrc =
+                __builtin_amdgcn_make_buffer_rsrc(obase, 0, rows_valid * ldo * 2, kBufferFlags);
+            constexpr int NQ = (EPI == Epi::kSwiGLU) ? 1 : 2;
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row within the 32-row block
+                        const float sr = srow[tm * 32 + rr];
+                        float v;
+                        if constexpr (EPI == Epi::kBf16) {
+                            v = (float)acc[tm][q][r];
+                            v = v * sr;
+                            v = v * cs[q];
+                            if (p.bias) v = v + bias[q];
+                        } else {
+                            float gt = (float)acc[tm][0][r];
+                            gt = gt * sr;
+                            gt = gt * cs[0];
+                            float up = (float)acc[tm][1][r];
+                            up = up * sr;
+                            up = up * cs[1];
+                            const float gb = bf16_to_float(float_to_bf16(gt));
+                            const float ub = bf16_to_float(float_to_bf16(up));
+                            v = silu_fixed(gb) * ub;
+                        }
+                        *reinterpret_cast<uint16_t*>(stg + swz_offset(rr, col >> 3) + (col & 7) * 2) =
+                            (uint16_t)float_to_bf16(v);
+                    }
+                    // the wavefront reads back its own block (one wavefront's LDS operations stay in order)
+                    const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32;  // first output column of the block
+                    if (vec_store) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int c = h * 64 + lane;  // 128 chunks: 32 rows x 4 chunks of 8 columns
+                            const int rr = c >> 2, ch = c & 3;
+                            const int row = mh * HALF + tm * 32 + rr;  // row within the tile
+                            const int cc = col0 + ch * 8;
+                            const v4i v = *reinterpret_cast<const v4i*>(stg + swz_offset(rr, ch));
+                            const int off = cc < ldo ? (row * ldo + cc) * 2 : kOobOffset;
+                            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
+                        }
+                        ops += 2;
+                    } else {
+                        // row length not a multiple of 8: element stores, left out of the count
+                        for (int c = lane; c < 32 * 32; c += 64) {
+                            const int rr = c >> 5, cx = c & 31;
+                            const int row = mh * HALF + tm * 32 + rr;
+                            const int cc = col0 + cx;
+                            if (row < rows_valid && cc < ldo)
+                                obase[(int64_t)row * ldo + cc] =
+                                    *reinterpret_cast<const uint16_t*>(stg + swz_offset(rr, cx >> 3) + (cx & 7) * 2);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // prologue: each ring fills all but one stage
+    for (int g = 0; g < S - 1; ++g) {
+        if (g < total_stages) issue(g);
+        hist[g] = ops;
+    }
+    clear_acc();
+
+    for (int g = 0; g < total_stages; ++g) {
+        const int i = g / nk, kt = g - i * nk;
+        // wait for this wavefront's loads of stage g; what it issued afterwards may stay in flight
+        wait_vmcnt_dyn(ops - hist[0]);
+        if constexpr (!TILED) {
+            if (b_loader) wait_lgkmcnt0();  // row-major weights reach the ring through ds_write
+        }
+        __builtin_amdgcn_s_barrier();  // stage g of both rings landed; everyone is done with stage g-1
+        // keeps the LDS reads of stage g below the barrier (costs an lgkmcnt wait, not a vmcnt one)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+        for (int s = 0; s + 2 < Cfg::SMAX; ++s)
+            if (s + 2 < S) hist[s] = hist[s + 1];
+        if (g + S - 1 < total_stages) issue(g + S - 1);
+        if (b_loader)
+            hist[SB - 2] = ops;
+        else
+            hist[SA - 2] = ops;
+        compute(g);
+        if (kt == nk - 1) {
+            epilogue(i, g);
+            clear_acc();
         }
     }
 }
 
-template <int BM, int S, int OCC, Epi EPI, int WBITS, bool TILED>
+template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
+    using Cfg = GemmCfg<BM, SB, SA, EPI, WBITS, TILED>;
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = (EPI == Epi::kSwiGLU) ? (p.N / 2 + kBN / 2 - 1) / (kBN / 2) : (p.N + kBN - 1) / kBN;
-    constexpr int stage = BM * kBK + 4 * ((WBITS == 8) ? 4 : 2) * 1024;
-    constexpr int out_stride = ((EPI == Epi::kSwiGLU) ? kBN / 2 : kBN) * 2 + 16;
-    constexpr int ring = (S * stage > BM * out_stride) ? S * stage : BM * out_stride;
-    const size_t lds = (size_t)ring + BM * sizeof(float);
-    auto kern = grouped_gemm_kernel<BM, S, OCC, EPI, WBITS, TILED>;
+    auto kern = grouped_gemm_kernel<BM, SB, SA, EPI, WBITS, TILED>;
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
     if (attr != hipSuccess) return attr;
     const int64_t total = (int64_t)p.E * tiles_m * tiles_n;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    kern<<<dim3((unsigned)total), dim3(kThreads), lds, st>>>(p, tiles_m, tiles_n);
+    const int64_t ldo = (EPI == Epi::kSwiGLU) ? p.N / 2 : p.N;
+    if ((int64_t)BM * ldo * 2 >= kOobOffset) return hipErrorInvalidValue;  // an output tile must fit one range
+    static int ncu_cache[64] = {0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    int ncu = (dev >= 0 && dev < 64) ? ncu_cache[dev] : 0;
+    if (ncu <= 0) {
+        err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        if (ncu <= 0) return hipErrorInvalidValue;
+        if (dev >= 0 && dev < 64) ncu_cache[dev] = ncu;
+    }
+    const int grid = (int)(total < ncu ? total : ncu);  // one persistent workgroup per CU
+    kern<<<dim3((unsigned)grid), dim3(kThreads), Cfg::LDS, st>>>(p, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 template <Epi EPI, int WBITS, bool TILED>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
-    // Two workgroups per CU in both shapes (LDS: 60 KiB and 72.5 KiB per workgroup).
-    if (p.M <= 64) return launch_cfg<64, 3, 2, EPI, WBITS, TILED>(p, st);
-    return launch_cfg<128, 3, 2, EPI, WBITS, TILED>(p, st);
+    // Weight ring depth: what the LDS leaves after the 3-stage activation ring; 4-bit weight stages are half
+    // the size, so about twice as many.
+    if constexpr (WBITS == 8) {
+        if (p.M <= 64) return launch_cfg<64, 8, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 128) return launch_cfg<128, 7, 3, EPI, WBITS, TILED>(p, st);
+        return launch_cfg<256, 6, 3, EPI, WBITS, TILED>(p, st);
+    } else {
+        if (p.M <= 64) return launch_cfg<64, 14, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 128) return launch_cfg<128, 13, 3, EPI, WBITS, TILED>(p, st);
+        return launch_cfg<256, 10, 3, EPI, WBITS, TILED>(p, st);
+    }
 }
 
 }  // namespace
