@@ -45,6 +45,7 @@ namespace crk {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -52,7 +53,6 @@ constexpr int kBK = 64;          // K bytes per pipeline stage (two MFMA slices)
 constexpr int kBN = 256;         // weight rows per tile (8 blocks of 32)
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStgBytes = 2048;           // per wavefront: one 32 x 32 bf16 block of the epilogue
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw (untyped) gfx9 buffer access
 constexpr int kOobOffset = 0x40000000;    // byte offset past every output range (the store is dropped)
 // Cache policy of the weight DMAs: non-temporal; streaming with nt measured ~6.5 TB/s vs ~5.7 TB/s without.
@@ -82,6 +82,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return float_to_bf16(lo) | (float_to_bf16(hi) << 16);
+}
+
 // vmcnt(x) for a wave-uniform x (binary search over the immediate forms; scalar branches only).
 template <int L, int H>
 __device__ __forceinline__ void wait_vmcnt_range(int x) {
@@ -110,12 +114,10 @@ struct GemmCfg {
     static constexpr int B_BYTES = NBT * 1024;
     static constexpr int B_RING = SB * B_BYTES;
     static constexpr int A_RING = SA * A_BYTES;
-    static constexpr bool STG_IN_RING = B_BYTES >= kWaves * kStgBytes;  // staging in the consumed weight slot
     static constexpr int CSC_OFF = B_RING + A_RING;          // SB slots of 256 column scales
     static constexpr int SROW_OFF = CSC_OFF + SB * kBN * 4;  // SA slots of BM row scales
     static constexpr int ROWS_OFF = SROW_OFF + SA * BM * 4;  // 2 slots of BM gathered row indices
-    static constexpr int STG_OFF = ROWS_OFF + 2 * BM * 4;
-    static constexpr int LDS = STG_OFF + (STG_IN_RING ? 0 : kWaves * kStgBytes);
+    static constexpr int LDS = ROWS_OFF + 2 * BM * 4;
     static constexpr int SMAX = SB > SA ? SB : SA;
     static_assert(BM == 64 || BM == 128 || BM == 256, "tile rows");
     static_assert(NAW >= 1 && NAW * 4096 == A_BYTES, "activation stage / loader mismatch");
@@ -354,113 +356,136 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s][tm], bf[s][q], acc[tm][q], 0, 0, 0);
+                    acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[s][q], af[s][tm], acc[tm][q], 0, 0, 0);
         // Scheduling order: every LDS read of the stage, then the MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + 2), 0);  // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * TM, 0);        // MFMAs
     };
 
-    // Epilogue of tile i, run at global stage g (its last).  Lane l holds column l % 32 and rows
-    // 8 (r / 4) + 4 (l / 32) + r % 4 of each 32 x 32 accumulator block.
-    auto epilogue = [&](int i, int g) {
+    // Epilogue of tile i.  The weights are the MFMA's first operand, so lane l holds activation row l % 32 of
+    // each 32 x 32 block and, in register 4 j + i, weight row (output column) 8 j + 4 (l / 32) + i: each lane
+    // owns runs of 4 consecutive output columns, stored as 8 bytes straight from registers, and the gate and
+    // up values of one output sit in the same lane.
+    auto epilogue = [&](int i) {
         int e, nt, mt;
         decode(i, e, nt, mt);
-        const int col = lane & 31;
+        const int h = lane >> 5;
         if constexpr (EPI == Epi::kI32) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
-                const int mbase = mt * BM + mh * HALF + tm * 32 + (lane >> 5) * 4;
+                const int m = mt * BM + mh * HALF + tm * 32 + (lane & 31);
+                if (m >= M) continue;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + col;
-                    if (n >= N) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int m = mbase + (r >> 2) * 8 + (r & 3);
-                        if (m < M) static_cast<int32_t*>(p.out)[((int64_t)e * M + m) * N + n] = acc[tm][q][r];
+                        const int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (n < N) static_cast<int32_t*>(p.out)[((int64_t)e * M + m) * N + n] = acc[tm][q][r];
                     }
                 }
             }
         } else {
-            // every wavefront is done with stage g, so its weight slot can hold the staging blocks; the next
-            // loads into that slot are issued after the following K-step's barrier
-            __builtin_amdgcn_s_barrier();
-            int8_t* stg = (Cfg::STG_IN_RING ? b_ring + (g % SB) * B_BYTES : smem + Cfg::STG_OFF) + wave * kStgBytes;
             const float* srow = srow_lds + (i % SA) * BM + mh * HALF;
             const float* csc = csc_lds + (i % SB) * kBN;
-            float cs[2], bias[2] = {0.0f, 0.0f};
-            cs[0] = csc[my_blk0 * 32 + col];
-            cs[1] = csc[my_blk1 * 32 + col];
-            if constexpr (EPI == Epi::kBf16) {
-                if (p.bias) {
+            const int ldo = (EPI == Epi::kSwiGLU) ? I : N;  // output row length (elements)
+            const int rows_valid = (M - mt * BM) < BM ? (M - mt * BM) : BM;
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<uint16_t*>(p.out) + ((int64_t)e * M + mt * BM) * ldo, 0, rows_valid * ldo * 2, kBufferFlags);
+            // column scales (and bias) of this wavefront's two weight blocks, per run j: 4 consecutive columns
+            float cs[2][16], bias[2][16];
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + col;
-                        n = n < N ? n : N - 1;
-                        bias[q] = bf16_to_float(p.bias[n]);
+            for (int q = 0; q < 2; ++q) {
+                const int blk = q ? my_blk1 : my_blk0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4i c4 = *reinterpret_cast<const v4i*>(csc + blk * 32 + 8 * j + 4 * h);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) cs[q][4 * j + x] = __int_as_float(c4[x]);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bias[q][r] = 0.0f;
+                if constexpr (EPI == Epi::kBf16) {
+                    if (p.bias) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            int n = wblk(blk, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            n = n < N ? n : N - 1;
+                            bias[q][r] = bf16_to_float(p.bias[n]);
+                        }
                     }
                 }
             }
-            const int ldo = (EPI == Epi::kSwiGLU) ? I : N;  // output row length (elements)
-            const int rows_valid = (M - mt * BM) < BM ? (M - mt * BM) : BM;
-            uint16_t* const obase = static_cast<uint16_t*>(p.out) + ((int64_t)e * M + mt * BM) * ldo;
-            const bool vec_store = (ldo & 7) == 0;
-            const __amdgpu_buffer_rsrc_t orsrc =
-                __builtin_amdgcn_make_buffer_rsrc(obase, 0, rows_valid * ldo * 2, kBufferFlags);
-            constexpr int NQ = (EPI == Epi::kSwiGLU) ? 1 : 2;
+            // Two runs j0 < j1 of 4 outputs each, per lane: lanes l and l + 32 hold the two halves of an 8-column
+            // chunk, so one swap between the lane halves hands lane l the whole chunk of run j0 and lane l + 32
+            // the whole chunk of run j1: one 16-byte store each.  Rows that are not 8-aligned fall back to
+            // element stores.  Every store is issued; out-of-range ones are dropped by the buffer range.
+            const bool vec = (ldo & 7) == 0;
+            auto store_pair = [&](int row, int col0, int j0, int j1, const float (&v0)[4], const float (&v1)[4]) {
+                if (vec) {
+                    const uint32_t a0 = pack_bf16x2(v0[0], v0[1]), a1 = pack_bf16x2(v0[2], v0[3]);
+                    const uint32_t b0 = pack_bf16x2(v1[0], v1[1]), b1 = pack_bf16x2(v1[2], v1[3]);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                    const int col = col0 - 4 * h + 8 * (h ? j1 : j0);  // first column of this lane's chunk
+                    const int off = col < ldo ? (row * ldo + col) * 2 : kOobOffset;
+                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, orsrc,
+                                                           off, 0, 0);
+                    ops += 1;
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int col = col0 + 8 * (u ? j1 : j0);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const int off = col + x < ldo ? (row * ldo + col + x) * 2 : kOobOffset;
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)float_to_bf16(u ? v1[x] : v0[x]), orsrc, off, 0,
+                                                                  0);
+                        }
+                    }
+                    ops += 8;
+                }
+            };
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
+                const float sx = srow[tm * 32 + (lane & 31)];
+                const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
+                if constexpr (EPI == Epi::kBf16) {
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) {
+                    for (int q = 0; q < 2; ++q) {
+                        const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 4 * h;
+                        float v[4][4];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row within the 32-row block
-                        const float sr = srow[tm * 32 + rr];
-                        float v;
-                        if constexpr (EPI == Epi::kBf16) {
-                            v = (float)acc[tm][q][r];
-                            v = v * sr;
-                            v = v * cs[q];
-                            if (p.bias) v = v + bias[q];
-                        } else {
-                            float gt = (float)acc[tm][0][r];
-                            gt = gt * sr;
-                            gt = gt * cs[0];
-                            float up = (float)acc[tm][1][r];
-                            up = up * sr;
-                            up = up * cs[1];
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) {
+                                float t = (float)acc[tm][q][4 * j + x];
+                                t = t * sx;
+                                t = t * cs[q][4 * j + x];
+                                if (p.bias) t = t + bias[q][4 * j + x];
+                                v[j][x] = t;
+                            }
+                        store_pair(row, col0, 0, 1, v[0], v[1]);
+                        store_pair(row, col0, 2, 3, v[2], v[3]);
+                    }
+                } else {
+                    const int col0 = wblk(my_blk0, nt) * 32 + 4 * h;  // gate block index = output column block
+                    float a[4][4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            float gt = (float)acc[tm][0][4 * j + x];
+                            gt = gt * sx;
+                            gt = gt * cs[0][4 * j + x];
+                            float up = (float)acc[tm][1][4 * j + x];
+                            up = up * sx;
+                            up = up * cs[1][4 * j + x];
                             const float gb = bf16_to_float(float_to_bf16(gt));
                             const float ub = bf16_to_float(float_to_bf16(up));
-                            v = silu_fixed(gb) * ub;
+                            a[j][x] = silu_fixed(gb) * ub;
                         }
-                        *reinterpret_cast<uint16_t*>(stg + swz_offset(rr, col >> 3) + (col & 7) * 2) =
-                            (uint16_t)float_to_bf16(v);
-                    }
-                    // the wavefront reads back its own block (one wavefront's LDS operations stay in order)
-                    const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32;  // first output column of the block
-                    if (vec_store) {
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const int c = h * 64 + lane;  // 128 chunks: 32 rows x 4 chunks of 8 columns
-                            const int rr = c >> 2, ch = c & 3;
-                            const int row = mh * HALF + tm * 32 + rr;  // row within the tile
-                            const int cc = col0 + ch * 8;
-                            const v4i v = *reinterpret_cast<const v4i*>(stg + swz_offset(rr, ch));
-                            const int off = cc < ldo ? (row * ldo + cc) * 2 : kOobOffset;
-                            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
-                        }
-                        ops += 2;
-                    } else {
-                        // row length not a multiple of 8: element stores, left out of the count
-                        for (int c = lane; c < 32 * 32; c += 64) {
-                            const int rr = c >> 5, cx = c & 31;
-                            const int row = mh * HALF + tm * 32 + rr;
-                            const int cc = col0 + cx;
-                            if (row < rows_valid && cc < ldo)
-                                obase[(int64_t)row * ldo + cc] =
-                                    *reinterpret_cast<const uint16_t*>(stg + swz_offset(rr, cx >> 3) + (cx & 7) * 2);
-                        }
-                    }
+                    store_pair(row, col0, 0, 1, a[0], a[1]);
+                    store_pair(row, col0, 2, 3, a[2], a[3]);
                 }
             }
         }
@@ -493,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
             hist[SA - 2] = ops;
         compute(g);
         if (kt == nk - 1) {
-            epilogue(i, g);
+            epilogue(i);
             clear_acc();
         }
     }
