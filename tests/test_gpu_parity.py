@@ -83,6 +83,24 @@ def test_rotq_bit_exact(g, K, rows):
     assert np.array_equal(host(q), rq)
 
 
+@pytest.mark.parametrize("g,K", [(64, 512), (64, 1536), (64, 4096), (256, 2048), (256, 4096), (256, 8192)])
+@pytest.mark.parametrize("rows", [1, 7, 37])
+def test_rotq_codes_only_bit_exact(g, K, rows):
+    """The codes-only path (no rotated values requested; the layer's own path), including rows whose scale
+    falls below and just above the threshold of the reciprocal-based division."""
+    say(f"rotq codes g={g} K={K} rows={rows}")
+    x = _special_rows(rows, K, 7000 + K + rows)
+    if rows >= 7:
+        f = synth.bf16_bits_to_f32(x).copy()
+        f[5] *= np.float32(2.0 ** -100)         # scale near 2^-107: IEEE division
+        f[6] *= np.float32(2.0 ** -80)          # scale near 2^-87: reciprocal-based division
+        x = synth.to_bf16_bits(f)
+    q, s, _ = cr.convrot_rotq_rows(dev_bf16(x), g)
+    rq, rs = oracle.rotq_rows(x, g)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+
+
 def test_rotq_zero_rows_is_noop():
     x = torch.zeros((0, 512), dtype=torch.bfloat16, device=DEV)
     q, s, _ = cr.convrot_rotq_rows(x, 64)

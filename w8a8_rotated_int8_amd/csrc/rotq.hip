@@ -201,6 +201,115 @@ __global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__
     if (lane == 0 && !pad) sout[row] = scale;
 }
 
+// ---- activation rows, fast path: K a multiple of 8 g ------------------------------------------------------
+// Lane l holds, in each of R = K / (8 g) rounds, the contiguous run of E = g / 8 elements
+// [round * 8g + l * E, + E): every g-block sits on 8 consecutive lanes, so the transform runs its stages
+// h < E inside the lane and only h = E, 2E, 4E across lanes (partner lane l ^ 1, ^ 2 via DPP quad
+// permutations, ^ 4 via a swizzle).  Every stage still forms the pairs (a + b, a - b) of the ascending-h
+// transform, so the fp32 values are those of the plain loop.
+//
+// Quantiser division: with y = 1 / scale rounded to nearest (one IEEE division per row), the quotient
+// q0 = r y, its exact remainder e = fma(-q0, scale, r) and q = fma(e, y, q0) give the correctly rounded
+// r / scale (Markstein's theorem; it needs the remainder to be exact, which holds while scale >= 2^-96 --
+// checked exhaustively on random and half-integer quotients over the whole fp32 range).  Smaller scales
+// take the IEEE division.
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+}
+__device__ __forceinline__ float swz_xor4(float v) {
+    // ds_swizzle bit-mask mode: and 0x1f, or 0, xor 4 (within 32 lanes)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+
+template <int G, int R>
+__global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __restrict__ x, int64_t rows, int K,
+                                                            int8_t* __restrict__ q, float* __restrict__ s) {
+    constexpr int E = G / 8;  // elements per lane per round
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const uint16_t* src = x + row * (int64_t)K + lane * E;
+    float v[R][E];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < E / 8; ++c) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[r][8 * c + 2 * e] = bf16_to_float(w[e] & 0xffffu);
+                v[r][8 * c + 2 * e + 1] = bf16_to_float(w[e] >> 16);
+            }
+        }
+    constexpr float kNorm = (G == 256) ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
+    const bool up1 = (lane & 1) != 0, up2 = (lane & 2) != 0, up4 = (lane & 4) != 0;
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int h = 1; h < E; h *= 2)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if ((e & h) == 0) {
+                    const float a = v[r][e], b = v[r][e + h];
+                    v[r][e] = a + b;
+                    v[r][e + h] = a - b;
+                }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float mine = v[r][e], other = dpp_xor1(mine);
+            mine = up1 ? (other - mine) : (mine + other);
+            other = dpp_xor2(mine);
+            mine = up2 ? (other - mine) : (mine + other);
+            other = swz_xor4(mine);
+            mine = up4 ? (other - mine) : (mine + other);
+            mine = mine * kNorm;
+            v[r][e] = mine;
+            amax = fmaxf(amax, fabsf(mine));
+        }
+    }
+    amax = wave_max(amax);
+    const float scale = amax / 127.0f;
+    const bool fast = scale >= 0x1p-96f;  // wave-uniform
+    const float y = fast ? 1.0f / scale : 0.0f;
+    int8_t* dst = q + row * (int64_t)K + lane * E;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t packed[E / 4];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float c;
+            if (fast) {
+                const float q0 = v[r][e] * y;
+                const float rem = __builtin_fmaf(-q0, scale, v[r][e]);
+                c = rintf(__builtin_fmaf(rem, y, q0));
+            } else {
+                c = scale == 0.0f ? 0.0f : rintf(v[r][e] / scale);
+            }
+            c = __builtin_amdgcn_fmed3f(c, -127.0f, 127.0f);
+            const uint32_t b = (uint32_t)((int)c & 0xff);
+            if (e % 4 == 0)
+                packed[e / 4] = b;
+            else
+                packed[e / 4] |= b << (8 * (e % 4));
+        }
+        if constexpr (E == 8) {
+            *reinterpret_cast<uint2*>(dst + r * 8 * G) = make_uint2(packed[0], packed[1]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < E / 16; ++c)
+                *reinterpret_cast<uint4*>(dst + r * 8 * G + 16 * c) =
+                    make_uint4(packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]);
+        }
+    }
+    if (lane == 0) s[row] = scale;
+}
+
 // rows: source rows (E * N for weights); N: rows per expert (tiled modes only).
 template <int G, int QMAX, Out OUT, bool CHECK>
 hipError_t launch_nv(const void* x, int64_t rows, int K, int N, void* q, float* s, float* rot, hipStream_t st) {
@@ -230,6 +339,25 @@ hipError_t launch_nv(const void* x, int64_t rows, int K, int N, void* q, float* 
 hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
                            hipStream_t st) {
     if (rows == 0) return hipSuccess;
+    if (rot == nullptr && K % (8 * group) == 0) {
+        const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+        const int R = K / (8 * group);
+#define CRK_FAST(G, RR)                                                                          \
+    if (group == G && R == RR) {                                                                 \
+        rotq_act_fast_kernel<G, RR><<<grid, block, 0, st>>>(x, rows, K, q, s);                   \
+        return hipGetLastError();                                                                \
+    }
+        CRK_FAST(256, 1)
+        CRK_FAST(256, 2)
+        CRK_FAST(256, 4)
+        CRK_FAST(64, 1)
+        CRK_FAST(64, 2)
+        CRK_FAST(64, 3)
+        CRK_FAST(64, 4)
+        CRK_FAST(64, 6)
+        CRK_FAST(64, 8)
+#undef CRK_FAST
+    }
     if (group == 256) return launch_nv<256, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
     return launch_nv<64, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
 }
