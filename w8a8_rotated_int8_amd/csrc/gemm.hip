@@ -32,10 +32,13 @@
 //     DMAs into an SA-deep ring.  A wavefront's vector memory operations complete in issue order, so waiting
 //     for vmcnt <= X, where X counts operations it issued after a stage, proves that the stage has landed.
 //     Every wavefront counts the operations it issues (DMAs, and the epilogue's buffer stores, which are
-//     always issued and drop out-of-range lanes in hardware) and waits with that exact X: the weight ring
-//     stays SB-1 stages ahead through tile boundaries and epilogues, the activation ring SA-1.  Operations
-//     left out of the count can only make a wait stricter.  One workgroup barrier per K-step publishes both
-//     rings.
+//     always issued and drop out-of-range lanes in hardware) and waits with that exact X, so each ring keeps
+//     its full depth in flight through tile boundaries and epilogues.  Operations left out of the count can
+//     only make a wait stricter.
+//   * Half steps: the MFMAs of a stage's first slice run while its second slice is read from LDS; then one
+//     workgroup barrier publishes the next stage (and frees the slots of this one for the loads S stages
+//     ahead), and the MFMAs of the second slice run while the first slice of the next stage is read.  The
+//     matrix pipe never waits for a whole stage of fragment reads.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
 #include "device_common.h"
@@ -114,14 +117,17 @@ struct GemmCfg {
     static constexpr int B_BYTES = NBT * 1024;
     static constexpr int B_RING = SB * B_BYTES;
     static constexpr int A_RING = SA * A_BYTES;
-    static constexpr int CSC_OFF = B_RING + A_RING;          // SB slots of 256 column scales
-    static constexpr int SROW_OFF = CSC_OFF + SB * kBN * 4;  // SA slots of BM row scales
-    static constexpr int ROWS_OFF = SROW_OFF + SA * BM * 4;  // 2 slots of BM gathered row indices
-    static constexpr int LDS = ROWS_OFF + 2 * BM * 4;
     static constexpr int SMAX = SB > SA ? SB : SA;
+    // A tile's scales are loaded with its first stage, up to SMAX stages before the tile starts, and read by
+    // its epilogue: SMAX + 1 slots keep them until then for any K.
+    static constexpr int NSC = SMAX + 1;
+    static constexpr int CSC_OFF = B_RING + A_RING;           // NSC slots of 256 column scales
+    static constexpr int SROW_OFF = CSC_OFF + NSC * kBN * 4;  // NSC slots of BM row scales
+    static constexpr int ROWS_OFF = SROW_OFF + NSC * BM * 4;  // 2 slots of BM gathered row indices
+    static constexpr int LDS = ROWS_OFF + 2 * BM * 4;
     static_assert(BM == 64 || BM == 128 || BM == 256, "tile rows");
     static_assert(NAW >= 1 && NAW * 4096 == A_BYTES, "activation stage / loader mismatch");
-    static_assert(SB >= 2 && SA >= 3, "ring depth");
+    static_assert(SB >= 3 && SA >= 3, "ring depth");
     static_assert(TILED || WBITS == 8, "4-bit weights are only stored tiled");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -153,8 +159,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     const int nk = (K + kBK - 1) / kBK;
     const int NBk = (N + 31) >> 5;  // row blocks per expert
     // Gathered row indices reach the activation loaders through LDS when the index DMA of tile i+1, issued
-    // with the first stage of tile i, is published by the time tile i+1's loads are issued (nk >= SA - 1).
-    const bool rows_via_lds = p.a_rows != nullptr && nk >= SA - 1;
+    // with the first stage of tile i, is published by the time tile i+1's loads are issued (nk >= SA).
+    const bool rows_via_lds = p.a_rows != nullptr && nk >= SA;
 
     // ---- this workgroup's tiles: XCD x owns the contiguous range [xs, xs + xn); its workgroups interleave ----
     const int total = p.E * tiles_m * tiles_n;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 int n = wblk(j, nt) * 32 + (lane & 31);
                 n = n < N ? n : N - 1;
                 __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.b_scale + (int64_t)e * N + n),
-                                                 (lds_void*)(csc_lds + (i % SB) * kBN + nq * 64), 4, 0, 0);
+                                                 (lds_void*)(csc_lds + (i % Cfg::NSC) * kBN + nq * 64), 4, 0, 0);
                 ++ops;
             }
         } else {
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 const int r = aw * 64 + lane;
                 if constexpr (kScales) {
                     __builtin_amdgcn_global_load_lds(static_cast<const void*>(p.a_scale + arow_of(r)),
-                                                     (lds_void*)(srow_lds + (i % SA) * BM + aw * 64), 4, 0, 0);
+                                                     (lds_void*)(srow_lds + (i % Cfg::NSC) * BM + aw * 64), 4, 0, 0);
                     ++ops;
                 }
                 if (rows_via_lds && i + 1 < my_tiles) {
@@ -279,12 +285,11 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         ld_tile = i;
     };
 
-    // Loads of global stage g (tile g / nk, K-step g % nk) into ring slot g % S of this wavefront's role.
-    auto issue = [&](int g) {
-        const int i = g / nk, kt = g - i * nk;
+    // Loads of stage (tile i, K-step kt) into ring slot `slot` of this wavefront's role.
+    auto issue = [&](int i, int kt, int slot) {
         if (i != ld_tile) set_loader_tile(i);
         if (b_loader) {
-            int8_t* st = b_ring + (g % SB) * B_BYTES;
+            int8_t* st = b_ring + slot * B_BYTES;
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
                 const int t = nq * NBW + j;
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 }
             }
         } else {
-            int8_t* st = a_ring + (g % SA) * A_BYTES;
+            int8_t* st = a_ring + slot * A_BYTES;
 #pragma unroll
             for (int j = 0; j < NAW; ++j) {
                 int k = kt * kBK + src_off[j];
@@ -325,41 +330,44 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 for (int r = 0; r < 16; ++r) acc[i][q][r] = 0;
     };
 
-    // All fragments of both slices are read first, so the LDS latency of later fragments hides under the
-    // MFMAs of earlier ones.
-    auto compute = [&](int g) {
-        const int8_t* As = a_ring + (g % SA) * A_BYTES;
-        const int8_t* Bs = b_ring + (g % SB) * B_BYTES + lane * 16;
-        v4i bf[2][2];
-        v4i af[2][TM];
+    // Fragments of one 32-deep slice s of the stage in ring slots (as, bs): this wavefront's two weight blocks
+    // and its TM activation row blocks.
+    auto read_slice = [&](int as, int bs, int s, v4i (&bf)[2], v4i (&af)[TM]) {
+        const int8_t* As = a_ring + as * A_BYTES;
+        const int8_t* Bs = b_ring + bs * B_BYTES + lane * 16;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int blk = q ? my_blk1 : my_blk0;
-                if constexpr (WBITS == 8) {
-                    bf[s][q] = *reinterpret_cast<const v4i*>(Bs + (2 * blk + s) * 1024);
-                } else {
-                    const uint2 w = *reinterpret_cast<const uint2*>(Bs + blk * 1024 + 8 * s);
-                    const uint2 u0 = unpack_nibbles(w.x), u1 = unpack_nibbles(w.y);
-                    bf[s][q] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
-                }
+        for (int q = 0; q < 2; ++q) {
+            const int blk = q ? my_blk1 : my_blk0;
+            if constexpr (WBITS == 8) {
+                bf[q] = *reinterpret_cast<const v4i*>(Bs + (2 * blk + s) * 1024);
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2*>(Bs + blk * 1024 + 8 * s);
+                const uint2 u0 = unpack_nibbles(w.x), u1 = unpack_nibbles(w.y);
+                bf[q] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
             }
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-                af[s][tm] = *reinterpret_cast<const v4i*>(
-                    As + swz_offset(mh * HALF + tm * 32 + (lane & 31), 2 * s + (lane >> 5)));
         }
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int tm = 0; tm < TM; ++tm)
+            af[tm] = *reinterpret_cast<const v4i*>(As + swz_offset(mh * HALF + tm * 32 + (lane & 31), 2 * s + (lane >> 5)));
+    };
+    auto mfma_slice = [&](const v4i (&bf)[2], const v4i (&af)[TM]) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
+        for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[s][q], af[s][tm], acc[tm][q], 0, 0, 0);
-        // Scheduling order: every LDS read of the stage, then the MFMAs.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + 2), 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * TM, 0);        // MFMAs
+            for (int q = 0; q < 2; ++q)
+                acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[q], af[tm], acc[tm][q], 0, 0, 0);
+    };
+    // Scheduling of a half step: the 2 * TM MFMAs of one slice alternate with the 2 + TM fragment reads of the
+    // next slice, so the matrix pipe is fed while the LDS delivers.
+    auto interleave = [&]() {
+        constexpr int kMfma = 2 * TM, kReads = 2 + TM, kPairs = kMfma < kReads ? kMfma : kReads;
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        if constexpr (kMfma > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
+        if constexpr (kReads > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairs, 0);
     };
 
     // Epilogue of tile i.  The weights are the MFMA's first operand, so lane l holds activation row l % 32 of
@@ -385,36 +393,31 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 }
             }
         } else {
-            const float* srow = srow_lds + (i % SA) * BM + mh * HALF;
-            const float* csc = csc_lds + (i % SB) * kBN;
+            const float* srow = srow_lds + (i % Cfg::NSC) * BM + mh * HALF;
+            const float* csc = csc_lds + (i % Cfg::NSC) * kBN;
             const int ldo = (EPI == Epi::kSwiGLU) ? I : N;  // output row length (elements)
             const int rows_valid = (M - mt * BM) < BM ? (M - mt * BM) : BM;
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                 static_cast<uint16_t*>(p.out) + ((int64_t)e * M + mt * BM) * ldo, 0, rows_valid * ldo * 2, kBufferFlags);
-            // column scales (and bias) of this wavefront's two weight blocks, per run j: 4 consecutive columns
-            float cs[2][16], bias[2][16];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            // column scales (and bias) of weight block q of this wavefront, per run j: 4 consecutive columns
+            auto load_cs = [&](int q, float (&c)[16]) {
                 const int blk = q ? my_blk1 : my_blk0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v4i c4 = *reinterpret_cast<const v4i*>(csc + blk * 32 + 8 * j + 4 * h);
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) cs[q][4 * j + x] = __int_as_float(c4[x]);
+                    for (int x = 0; x < 4; ++x) c[4 * j + x] = __int_as_float(c4[x]);
                 }
+            };
+            auto load_bias = [&](int q, float (&b)[16]) {
+                const int blk = q ? my_blk1 : my_blk0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) bias[q][r] = 0.0f;
-                if constexpr (EPI == Epi::kBf16) {
-                    if (p.bias) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            int n = wblk(blk, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            n = n < N ? n : N - 1;
-                            bias[q][r] = bf16_to_float(p.bias[n]);
-                        }
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    int n = wblk(blk, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    n = n < N ? n : N - 1;
+                    b[r] = p.bias ? bf16_to_float(p.bias[n]) : 0.0f;
                 }
-            }
+            };
             // Two runs j0 < j1 of 4 outputs each, per lane: lanes l and l + 32 hold the two halves of an 8-column
             // chunk, so one swap between the lane halves hands lane l the whole chunk of run j0 and lane l + 32
             // the whole chunk of run j1: one 16-byte store each.  Rows that are not 8-aligned fall back to
@@ -445,14 +448,18 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                     ops += 8;
                 }
             };
+            if constexpr (EPI == Epi::kBf16) {
+                // weight block outer, so only one block's scales and bias are live
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const float sx = srow[tm * 32 + (lane & 31)];
-                const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
-                if constexpr (EPI == Epi::kBf16) {
+                for (int q = 0; q < 2; ++q) {
+                    float cs[16], bias[16];
+                    load_cs(q, cs);
+                    load_bias(q, bias);
+                    const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 4 * h;
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 4 * h;
+                    for (int tm = 0; tm < TM; ++tm) {
+                        const float sx = srow[tm * 32 + (lane & 31)];
+                        const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
                         float v[4][4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
@@ -460,15 +467,23 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                             for (int x = 0; x < 4; ++x) {
                                 float t = (float)acc[tm][q][4 * j + x];
                                 t = t * sx;
-                                t = t * cs[q][4 * j + x];
-                                if (p.bias) t = t + bias[q][4 * j + x];
+                                t = t * cs[4 * j + x];
+                                if (p.bias) t = t + bias[4 * j + x];
                                 v[j][x] = t;
                             }
                         store_pair(row, col0, 0, 1, v[0], v[1]);
                         store_pair(row, col0, 2, 3, v[2], v[3]);
                     }
-                } else {
-                    const int col0 = wblk(my_blk0, nt) * 32 + 4 * h;  // gate block index = output column block
+                }
+            } else {
+                float cg[16], cu[16];
+                load_cs(0, cg);
+                load_cs(1, cu);
+                const int col0 = wblk(my_blk0, nt) * 32 + 4 * h;  // gate block index = output column block
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const float sx = srow[tm * 32 + (lane & 31)];
+                    const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
                     float a[4][4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
@@ -476,10 +491,10 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                         for (int x = 0; x < 4; ++x) {
                             float gt = (float)acc[tm][0][4 * j + x];
                             gt = gt * sx;
-                            gt = gt * cs[0][4 * j + x];
+                            gt = gt * cg[4 * j + x];
                             float up = (float)acc[tm][1][4 * j + x];
                             up = up * sx;
-                            up = up * cs[1][4 * j + x];
+                            up = up * cu[4 * j + x];
                             const float gb = bf16_to_float(float_to_bf16(gt));
                             const float ub = bf16_to_float(float_to_bf16(up));
                             a[j][x] = silu_fixed(gb) * ub;
@@ -491,37 +506,89 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         }
     };
 
-    // prologue: each ring fills all but one stage
-    for (int g = 0; g < S - 1; ++g) {
-        if (g < total_stages) issue(g);
-        hist[g] = ops;
+    // ---- the pipeline ----
+    // Stage g is consumed in two half steps.  Half step A: MFMAs of slice 0 while slice 1 is read from LDS.
+    // Then the wavefront waits for its own loads of stage g+1 and for its LDS reads, and the workgroup barrier
+    // publishes stage g+1 and frees the slots of stage g, which take the loads of stage g+S.  Half step B:
+    // MFMAs of slice 1 while slice 0 of stage g+1 is read.  Every ring keeps S stages in flight.
+    int ld_i = 0, ld_kt = 0, ld_slot = 0, ld_left = total_stages;  // next stage to issue
+    auto issue_next = [&]() {
+        if (ld_left <= 0) return;
+        issue(ld_i, ld_kt, ld_slot);
+        --ld_left;
+        if (++ld_kt == nk) {
+            ld_kt = 0;
+            ++ld_i;
+        }
+        ld_slot = (ld_slot + 1 == S) ? 0 : ld_slot + 1;
+    };
+    // vmcnt that proves this wavefront's loads of a stage landed: x operations were issued after them.  In the
+    // steady state x is the loads of S - 2 stages; otherwise the exact count goes through the general form.
+    constexpr int kSteadyB = (SB - 2) * NBW;
+    constexpr int kSteadyA = (SA - 2) * NAW;
+    auto wait_landed = [&](int x) {
+        if (b_loader && TILED && x == kSteadyB)
+            wait_vmcnt<kSteadyB>();
+        else if (!b_loader && x == kSteadyA)
+            wait_vmcnt<kSteadyA>();
+        else
+            wait_vmcnt_dyn(x);
+    };
+
+    // prologue: every ring slot takes a stage; hist[t] = operations issued up to the end of stage t
+#pragma unroll
+    for (int t = 0; t < Cfg::SMAX; ++t) {
+        if (t < S) issue_next();
+        hist[t] = ops;
     }
     clear_acc();
-
-    for (int g = 0; g < total_stages; ++g) {
-        const int i = g / nk, kt = g - i * nk;
-        // wait for this wavefront's loads of stage g; what it issued afterwards may stay in flight
-        wait_vmcnt_dyn(ops - hist[0]);
-        if constexpr (!TILED) {
-            if (b_loader) wait_lgkmcnt0();  // row-major weights reach the ring through ds_write
-        }
-        __builtin_amdgcn_s_barrier();  // stage g of both rings landed; everyone is done with stage g-1
-        // keeps the LDS reads of stage g below the barrier (costs an lgkmcnt wait, not a vmcnt one)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    wait_landed(ops - hist[0]);
+    if constexpr (!TILED) {
+        if (b_loader) wait_lgkmcnt0();  // row-major weights reach the ring through ds_write
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
-        for (int s = 0; s + 2 < Cfg::SMAX; ++s)
-            if (s + 2 < S) hist[s] = hist[s + 1];
-        if (g + S - 1 < total_stages) issue(g + S - 1);
+    for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];  // hist[j]: end of stage g + 1 + j
+
+    v4i bf0[2], af0[TM], bf1[2], af1[TM];
+    int a_slot = 0, b_slot = 0, ci = 0, ckt = 0;
+    read_slice(0, 0, 0, bf0, af0);
+    for (int g = 0; g + 1 < total_stages; ++g) {
+        // half step A: slice 0 of stage g with the reads of slice 1
+        read_slice(a_slot, b_slot, 1, bf1, af1);
+        mfma_slice(bf0, af0);
+        interleave();
+        wait_landed(ops - hist[0]);  // this wavefront's part of stage g + 1
+        wait_lgkmcnt0();             // its reads of stage g (and any row-major ds_write)
+        __builtin_amdgcn_s_barrier();
+        // keeps the LDS reads of stage g + 1 below the barrier (costs an lgkmcnt wait, not a vmcnt one)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        a_slot = (a_slot + 1 == SA) ? 0 : a_slot + 1;
+        b_slot = (b_slot + 1 == SB) ? 0 : b_slot + 1;
+        // half step B: slice 1 of stage g with the reads of slice 0 of stage g + 1
+        read_slice(a_slot, b_slot, 0, bf0, af0);
+        mfma_slice(bf1, af1);
+        interleave();
+#pragma unroll
+        for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];
+        issue_next();  // stage g + S into the slots of stage g
         if (b_loader)
             hist[SB - 2] = ops;
         else
             hist[SA - 2] = ops;
-        compute(g);
-        if (kt == nk - 1) {
-            epilogue(i);
+        if (++ckt == nk) {
+            epilogue(ci);
             clear_acc();
+            ckt = 0;
+            ++ci;
         }
     }
+    // last stage (always the last K-step of the last tile)
+    read_slice(a_slot, b_slot, 1, bf1, af1);
+    mfma_slice(bf0, af0);
+    mfma_slice(bf1, af1);
+    epilogue(ci);
 }
 
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
