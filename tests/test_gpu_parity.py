@@ -187,7 +187,8 @@ def test_linear_bit_exact(M, K, N, g, with_bias):
 # Routing
 # ----------------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T,E,C", [(300, 16, 1), (300, 16, 17), (300, 16, 300), (2048, 64, 64), (5000, 8, 1234)])
+@pytest.mark.parametrize("T,E,C", [(300, 16, 1), (300, 16, 17), (300, 16, 300), (2048, 64, 64), (5000, 8, 1234),
+                                   (1001, 48, 100), (8192, 64, 256), (13000, 16, 777), (20000, 8, 5000)])
 def test_route_from_logits_bit_exact(T, E, C):
     say(f"route T={T} E={E} C={C}")
     lg = synth.logits(T + E, T, E)

@@ -225,6 +225,19 @@ __device__ __forceinline__ float swz_xor4(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
 }
 
+// Code byte of a quotient t with |t| <= 127.5: clamp to [-127, 127], then adding 1.5 * 2^23 rounds to the
+// nearest integer (ties to even, as rint) and leaves it in the low mantissa bits, whose low byte is the code
+// in two's complement.
+__device__ __forceinline__ uint32_t code_bits(float t) {
+    return __float_as_uint(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f) + 12582912.0f);
+}
+// Low bytes of four such words, packed in order.
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // bytes: a0, b0, 0, 0
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // bytes: 0, 0, c0, d0
+    return ab | cd;
+}
+
 template <int G, int R>
 __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __restrict__ x, int64_t rows, int K,
                                                             int8_t* __restrict__ q, float* __restrict__ s) {
@@ -243,11 +256,13 @@ __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __re
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 v[r][8 * c + 2 * e] = bf16_to_float(w[e] & 0xffffu);
-                v[r][8 * c + 2 * e + 1] = bf16_to_float(w[e] >> 16);
+                v[r][8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
             }
         }
     constexpr float kNorm = (G == 256) ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
-    const bool up1 = (lane & 1) != 0, up2 = (lane & 2) != 0, up4 = (lane & 4) != 0;
+    // Across lanes the pair (a + b, a - b) is other + sgn * mine: the lower lane of a pair adds, the upper
+    // lane subtracts its own value from its partner's (multiplying by +-1 is exact, the fma rounds once).
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f, sg4 = (lane & 4) ? -1.0f : 1.0f;
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -262,42 +277,19 @@ __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __re
                 }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            float mine = v[r][e], other = dpp_xor1(mine);
-            mine = up1 ? (other - mine) : (mine + other);
-            other = dpp_xor2(mine);
-            mine = up2 ? (other - mine) : (mine + other);
-            other = swz_xor4(mine);
-            mine = up4 ? (other - mine) : (mine + other);
+            float mine = v[r][e];
+            mine = __builtin_fmaf(sg1, mine, dpp_xor1(mine));
+            mine = __builtin_fmaf(sg2, mine, dpp_xor2(mine));
+            mine = __builtin_fmaf(sg4, mine, swz_xor4(mine));
             mine = mine * kNorm;
             v[r][e] = mine;
             amax = fmaxf(amax, fabsf(mine));
         }
     }
-    amax = wave_max(amax);
+    amax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(amax))));  // wave-uniform
     const float scale = amax / 127.0f;
-    const bool fast = scale >= 0x1p-96f;  // wave-uniform
-    const float y = fast ? 1.0f / scale : 0.0f;
     int8_t* dst = q + row * (int64_t)K + lane * E;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        uint32_t packed[E / 4];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float c;
-            if (fast) {
-                const float q0 = v[r][e] * y;
-                const float rem = __builtin_fmaf(-q0, scale, v[r][e]);
-                c = rintf(__builtin_fmaf(rem, y, q0));
-            } else {
-                c = scale == 0.0f ? 0.0f : rintf(v[r][e] / scale);
-            }
-            c = __builtin_amdgcn_fmed3f(c, -127.0f, 127.0f);
-            const uint32_t b = (uint32_t)((int)c & 0xff);
-            if (e % 4 == 0)
-                packed[e / 4] = b;
-            else
-                packed[e / 4] |= b << (8 * (e % 4));
-        }
+    auto store_round = [&](int r, const uint32_t (&packed)[E / 4]) {
         if constexpr (E == 8) {
             *reinterpret_cast<uint2*>(dst + r * 8 * G) = make_uint2(packed[0], packed[1]);
         } else {
@@ -305,6 +297,38 @@ __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __re
             for (int c = 0; c < E / 16; ++c)
                 *reinterpret_cast<uint4*>(dst + r * 8 * G + 16 * c) =
                     make_uint4(packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]);
+        }
+    };
+    if (scale >= 0x1p-96f) {
+        const float y = 1.0f / scale;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t packed[E / 4];
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                uint32_t b[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float q0 = v[r][e + u] * y;
+                    const float rem = __builtin_fmaf(-q0, scale, v[r][e + u]);
+                    b[u] = code_bits(__builtin_fmaf(rem, y, q0));
+                }
+                packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
+            }
+            store_round(r, packed);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t packed[E / 4];
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                uint32_t b[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) b[u] = code_bits(scale == 0.0f ? 0.0f : v[r][e + u] / scale);
+                packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
+            }
+            store_round(r, packed);
         }
     }
     if (lane == 0) s[row] = scale;

@@ -2,12 +2,13 @@
 //
 //  softmax_t     p[t, :] = softmax over experts in fp32 (max-subtracted, the fixed exponential, sum in
 //                ascending expert order, one IEEE division per entry), written transposed as probs_t[e, t]
-//                so that each expert's column is contiguous.  E <= 64: a workgroup stages a 64-token x E
-//                tile of logits in LDS (coalesced loads), splits the exponentials and divisions over its
-//                four wavefronts, and keeps the sequential sum in one lane per token.
-//  select_topc   one workgroup per expert: radix select (four 8-bit passes, most significant first) of the
-//                C-th largest key over keys held in registers, then one ordered compaction (a workgroup
-//                scan of per-thread counts) that keeps every token above the threshold and the lowest-index
+//                so that each expert's column is contiguous.  E <= 64: a workgroup takes a 32-token x E tile
+//                of logits through LDS (coalesced 16-byte loads); eight lanes per token share the max, the
+//                exponentials and the divisions, one lane keeps the sequential sum, and the probabilities
+//                leave through a transposed LDS tile as 16-byte row stores.
+//  select_topc   one workgroup per expert: radix select (passes of up to 11 bits, most significant first,
+//                after the bits every key shares) of the C-th largest key over keys held in registers, then
+//                one ordered compaction that keeps every token above the threshold and the lowest-index
 //                tokens equal to it.  The list comes out in ascending token order without a sort; ties go
 //                to the lower token index by construction.
 //  build_slotmap per expert: slotmap[e, t] = position of t in expert e's list, or -1.
@@ -25,55 +26,96 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 }
 
 // ---- softmax, E <= 64 ----------------------------------------------------------------------------------
-constexpr int kSmTok = 64;     // tokens per workgroup
-constexpr int kSmStride = 65;  // LDS row stride (floats): lane t reads row t without bank conflicts
+// 32 tokens per 256-thread workgroup; thread (token tok = tid / 8, expert group eg = tid % 8) owns experts
+// 8 eg .. 8 eg + 7 of its token, so a token's eight threads are neighbouring lanes of one wavefront.
+constexpr int kSmTok = 32;
+constexpr int kSmStride = 65;           // LDS row stride of the [token][expert] tile (floats)
+constexpr int kSmTrStride = kSmTok + 1;  // LDS row stride of the [expert][token] tile
 
 __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
                                                               float* __restrict__ probs_t, float* __restrict__ probs_out) {
-    __shared__ float tile[kSmTok * kSmStride];  // logits, then exponentials, then probabilities
-    __shared__ float rowmax[4][kSmTok];
-    __shared__ float rowsum[kSmTok];
+    __shared__ float tile[kSmTok * kSmStride];  // logits, then exponentials
+    __shared__ float tr[64 * kSmTrStride];      // probabilities, transposed
+    __shared__ float zrow[kSmTok];
     const int t0 = blockIdx.x * kSmTok;
     const int ntok = (T - t0) < kSmTok ? (T - t0) : kSmTok;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, tok = tid >> 3, eg = tid & 7;
     const float* src = in + (int64_t)t0 * E;
-    for (int r = wave; r < ntok; r += 4)  // one coalesced row of E <= 64 floats per wavefront instruction
-        if (lane < E) tile[r * kSmStride + lane] = src[(int64_t)r * E + lane];
-    __syncthreads();
-    // experts handled by this wavefront: e = wave, wave + 4, ...
-    if (!is_probs) {
-        if (lane < ntok) {
-            const float* row = tile + lane * kSmStride;
-            float m = -__builtin_inff();
-            for (int e = wave; e < E; e += 4) m = fmaxf(m, row[e]);
-            rowmax[wave][lane] = m;
+    const int n = ntok * E;  // the tile is contiguous in global memory
+    if (E == 64 && ntok == kSmTok && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int f = tid + 256 * k;  // float4 index: row f / 16, columns 4 (f % 16) ..
+            const float4 v = reinterpret_cast<const float4*>(src)[f];
+            float* d = tile + (f >> 4) * kSmStride + 4 * (f & 15);
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
         }
-        __syncthreads();
-        if (lane < ntok) {
-            float* row = tile + lane * kSmStride;
-            const float m = fmaxf(fmaxf(rowmax[0][lane], rowmax[1][lane]), fmaxf(rowmax[2][lane], rowmax[3][lane]));
-            for (int e = wave; e < E; e += 4) row[e] = exp_fixed(row[e] - m);
+    } else {
+        for (int i = tid; i < n; i += 256) {
+            const int r = i / E;
+            tile[r * kSmStride + (i - r * E)] = src[i];
         }
-        __syncthreads();
-        if (wave == 0 && lane < ntok) {
-            const float* row = tile + lane * kSmStride;
-            float z = 0.0f;
-            for (int e = 0; e < E; ++e) z = z + row[e];  // ascending expert order
-            rowsum[lane] = z;
-        }
-        __syncthreads();
-        if (lane < ntok) {
-            float* row = tile + lane * kSmStride;
-            const float z = rowsum[lane];
-            for (int e = wave; e < E; e += 4) row[e] = row[e] / z;
-        }
-        __syncthreads();
     }
-    if (lane < ntok)
-        for (int e = wave; e < E; e += 4) probs_t[(int64_t)e * T + t0 + lane] = tile[lane * kSmStride + e];
-    if (probs_out)
-        for (int r = wave; r < ntok; r += 4)
-            if (lane < E) probs_out[(int64_t)(t0 + r) * E + lane] = tile[r * kSmStride + lane];
+    __syncthreads();
+    const bool tv = tok < ntok;
+    float* row = tile + tok * kSmStride;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (tv && 8 * eg + k < E) ? row[8 * eg + k] : -__builtin_inff();
+    if (!is_probs) {
+        float m = v[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) m = fmaxf(m, v[k]);
+        m = fmaxf(m, __shfl_xor(m, 1));  // the token's eight lanes
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v[k] = (8 * eg + k < E) ? exp_fixed(v[k] - m) : 0.0f;
+            if (tv && 8 * eg + k < E) row[8 * eg + k] = v[k];
+        }
+        __syncthreads();
+        if (eg == 0 && tv) {
+            float z = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 64; ++e)
+                if (e < E) z = z + row[e];  // ascending expert order
+            zrow[tok] = z;
+        }
+        __syncthreads();
+        const float z = zrow[tok];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = v[k] / z;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if (tv && 8 * eg + k < E) tr[(8 * eg + k) * kSmTrStride + tok] = v[k];
+    if (probs_out && tv) {
+        float* o = probs_out + (int64_t)(t0 + tok) * E;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (8 * eg + k < E) o[8 * eg + k] = v[k];
+    }
+    __syncthreads();
+    // probs_t rows: float4 f covers expert f / 8, tokens 4 (f % 8) .. + 3 of this tile
+    if (ntok == kSmTok && (T & 3) == 0 && (reinterpret_cast<uintptr_t>(probs_t) & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int f = tid + 256 * k, e = f >> 3, c = 4 * (f & 7);
+            if (e < E) {
+                const float* a = tr + e * kSmTrStride + c;
+                *reinterpret_cast<float4*>(probs_t + (int64_t)e * T + t0 + c) = make_float4(a[0], a[1], a[2], a[3]);
+            }
+        }
+    } else {
+        for (int i = tid; i < E * kSmTok; i += 256) {
+            const int e = i / kSmTok, c = i - e * kSmTok;
+            if (c < ntok) probs_t[(int64_t)e * T + t0 + c] = tr[e * kSmTrStride + c];
+        }
+    }
 }
 
 // ---- softmax, any E (one thread per token) ------------------------------------------------------------
@@ -128,144 +170,243 @@ __device__ __forceinline__ int block_excl_sum(int v, int* scratch, int& total) {
     return before + incl - v;
 }
 
-// Radix select: the key v with #(key > v) < C <= #(key >= v); returns v and sets need_eq = C - #(key > v).
-// The leading bits all keys share (from the workgroup min and max) are skipped, so the passes work on bits
-// that actually differ: softmax probabilities share their sign and high exponent bits, and a first pass
-// over those would pile every key into one or two histogram bins.
-template <int KPT>
-__device__ uint32_t radix_select(const uint32_t (&key)[KPT], const bool (&valid)[KPT], int C, uint32_t* hist,
-                                 uint32_t* s_prefix, uint32_t* s_remaining, uint32_t* s_minmax, int& need_eq) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
+// Keys in registers, eight wavefronts per expert: wavefront w owns tokens [256 KR w, 256 KR (w + 1)), lane l
+// the four tokens 256 j + 4 l .. + 3 of round j.  Radix passes of up to 11 bits (2048 LDS bins, one scan by
+// wavefront 0); the compaction needs one exchange of per-wavefront counts: a selected token's slot is
+// (# greater keys before it) + min(# equal keys before it, C - # greater keys overall), and both prefixes come
+// from ballots within a round.
+constexpr int kSelV = 8;  // wavefronts per workgroup
+
+// Wavefront-wide min / max / sum of a uint32 through DPP (quad permutations and row rotations reduce each
+// 16-lane row) and four lane reads; the result is wave-uniform.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t umin2(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umax2(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t uadd2(uint32_t a, uint32_t b) { return a + b; }
+
+// Inclusive prefix sum over the wavefront's lanes: row_shr 1, 2, 4, 8 within each 16-lane row, then the row
+// totals carried by row_bcast:15 and row_bcast:31 (lanes without a source add 0).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Sum over the lanes below this one of a per-lane count in [0, 7], and the total over the wavefront.
+__device__ __forceinline__ int lanes_below(int v, int& total) {
+    const uint64_t b0 = __ballot(v & 1), b1 = __ballot(v & 2), b2 = __ballot(v & 4);
+    total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+    auto below = [](uint64_t b) {
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+    };
+    return below(b0) + 2 * below(b1) + 4 * below(b2);
+}
+
+template <int KR>
+__global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
+                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
+                                                                   int32_t* __restrict__ slotmap) {
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ uint32_t s_red[2 * kSelV];
+    __shared__ uint32_t s_bcast[2];
+    __shared__ int s_cnt[2 * kSelV];
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float* p = probs_t + (int64_t)e * T;
+    const int tb = w * 256 * KR + 4 * lane;  // token of (round j, c): tb + 256 j + c
+    const bool vec = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+    // Up to 8 rounds the values stay in registers for the weights of the selected tokens; beyond that a
+    // selected token's value comes back from its key (invertible apart from the sign of zero, so a selected
+    // zero is read again).
+    constexpr bool kKeepVal = KR <= 8;
+    uint32_t key[KR][4];
+    float val[kKeepVal ? KR : 1][4];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-        if (valid[j]) {
-            kmin = key[j] < kmin ? key[j] : kmin;
-            kmax = key[j] > kmax ? key[j] : kmax;
+    for (int j = 0; j < KR; ++j) {
+        const int t = tb + 256 * j;
+        float f[4];
+        if (vec && t < T) {
+            const float4 q = *reinterpret_cast<const float4*>(p + t);
+            f[0] = q.x;
+            f[1] = q.y;
+            f[2] = q.z;
+            f[3] = q.w;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f[c] = (t + c < T) ? p[t + c] : 0.0f;
         }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
+        for (int c = 0; c < 4; ++c) {
+            key[j][c] = orderable(f[c]);
+            if constexpr (kKeepVal) val[j][c] = f[c];
+        }
     }
+    // Tokens past T hold key 0, the smallest key there is: they only add to the lowest bins, never exceed the
+    // threshold, and as equal keys they come after every real token, so they change no decision (C <= T).
+
+    // leading bits shared by every key (skipped by the passes)
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            kmin = key[j][c] < kmin ? key[j][c] : kmin;
+            kmax = key[j][c] > kmax ? key[j][c] : kmax;
+        }
+    kmin = wave_reduce_u32(kmin, umin2);
+    kmax = wave_reduce_u32(kmax, umax2);
     if (lane == 0) {
-        s_minmax[2 * wave] = kmin;
-        s_minmax[2 * wave + 1] = kmax;
+        s_red[2 * w] = kmin;
+        s_red[2 * w + 1] = kmax;
     }
     __syncthreads();
-    kmin = 0xffffffffu;
-    kmax = 0u;
-    for (int w = 0; w < kSelWaves; ++w) {
-        kmin = s_minmax[2 * w] < kmin ? s_minmax[2 * w] : kmin;
-        kmax = s_minmax[2 * w + 1] > kmax ? s_minmax[2 * w + 1] : kmax;
+#pragma unroll
+    for (int x = 0; x < kSelV; ++x) {
+        kmin = s_red[2 * x] < kmin ? s_red[2 * x] : kmin;
+        kmax = s_red[2 * x + 1] > kmax ? s_red[2 * x + 1] : kmax;
     }
     const uint32_t diff = kmin ^ kmax;
-    const int common = diff ? __clz(diff) : 32;  // leading bits shared by every key
+    const int common = diff ? __clz(diff) : 32;
     uint32_t mask = common ? (0xffffffffu << (32 - common)) : 0u;
     uint32_t prefix = kmin & mask, remaining = (uint32_t)C;
     for (int hi = 32 - common; hi > 0;) {  // bits [0, hi) still undecided
-        const int width = hi < 8 ? hi : 8;
+        const int width = hi < 11 ? hi : 11;
         const int shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
         hi = shift;
-        __syncthreads();
-        if (tid < 256) hist[tid] = 0;
+        __syncthreads();  // the previous scan is done with the bins
+#pragma unroll
+        for (int k = 0; k < 2; ++k) reinterpret_cast<uint4*>(hist)[tid + 256 * k] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (valid[j] && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
-        __syncthreads();
-        if (tid < 64) {
-            // lane l covers bins 255-4l .. 252-4l (descending); find the bin where the count from the top
-            // reaches `remaining`.
-            uint32_t c[4], sum = 0;
+        for (int j = 0; j < KR; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                c[q] = hist[255 - 4 * lane - q];
-                sum += c[q];
+            for (int c = 0; c < 4; ++c)
+                if ((key[j][c] & mask) == prefix) atomicAdd(&hist[(key[j][c] >> shift) & dmask], 1u);
+        __syncthreads();
+        if (w == 0) {
+            // lane l covers bins 2047 - 32 l down to 2016 - 32 l
+            uint32_t cnt[32], sum = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint4 q = reinterpret_cast<const uint4*>(hist)[(2016 - 32 * lane) / 4 + k];
+                cnt[31 - 4 * k] = q.x;
+                cnt[30 - 4 * k] = q.y;
+                cnt[29 - 4 * k] = q.z;
+                cnt[28 - 4 * k] = q.w;
             }
-            uint32_t incl = sum;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
+            for (int q = 0; q < 32; ++q) sum += cnt[q];
+            const uint32_t incl = wave_incl_sum(sum);
             const uint64_t hit = __ballot(incl >= remaining);
             const int first = __ffsll((unsigned long long)hit) - 1;
-            if (lane == first) {
-                uint32_t above = incl - sum;
-                int digit = 0;
+            // in lane `first`: the bins (descending) whose running count stays below `remaining` come before
+            // the digit's bin; the running count is monotone, so they are a prefix (no branches)
+            uint32_t cum = incl - sum, above = cum;
+            int nb = 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (above + c[q] >= remaining) {
-                        digit = 255 - 4 * lane - q;
-                        break;
-                    }
-                    above += c[q];
-                }
-                *s_prefix = prefix | ((uint32_t)digit << shift);
-                *s_remaining = remaining - above;
+            for (int q = 0; q < 32; ++q) {
+                cum += cnt[q];
+                const bool below = cum < remaining;
+                nb += below ? 1 : 0;
+                above += below ? cnt[q] : 0u;
+            }
+            if (lane == first) {
+                const int digit = 2047 - 32 * lane - nb;
+                s_bcast[0] = prefix | ((uint32_t)digit << shift);
+                s_bcast[1] = remaining - above;
             }
         }
         __syncthreads();
-        prefix = *s_prefix;
-        remaining = *s_remaining;
+        prefix = s_bcast[0];
+        remaining = s_bcast[1];
         mask |= dmask << shift;
     }
-    need_eq = (int)remaining;
-    return prefix;
-}
+    const uint32_t v = prefix;        // the C-th largest key
+    const int need_eq = (int)remaining;  // equal keys to take, lowest token index first
 
-// Keys in registers: thread tid owns tokens tid*KPT .. tid*KPT + KPT - 1 (requires T <= 1024 * KPT).
-template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void select_topc_reg_kernel(const float* __restrict__ probs_t, int T, int C,
-                                                                      int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                      int32_t* __restrict__ slotmap) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_prefix, s_remaining;
-    __shared__ uint32_t s_minmax[2 * kSelWaves];
-    __shared__ int scratch[kSelWaves];
-    const int e = blockIdx.x;
-    const int tid = threadIdx.x;
-    const float* p = probs_t + (int64_t)e * T;
-    const int tb = tid * KPT;
-    float pv[KPT];
-    uint32_t key[KPT];
-    bool valid[KPT];
+    // per-wavefront counts of equal and greater keys, then this wavefront's bases
+    int n_eq = 0, n_gt = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        valid[j] = tb + j < T;
-        pv[j] = valid[j] ? p[tb + j] : 0.0f;
-        key[j] = orderable(pv[j]);
-    }
-    int need_eq;
-    const uint32_t v = radix_select<KPT>(key, valid, C, hist, &s_prefix, &s_remaining, s_minmax, need_eq);
-
-    int n_eq = 0;
+    for (int j = 0; j < KR; ++j)
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) n_eq += (valid[j] && key[j] == v) ? 1 : 0;
-    int tot;
-    int eq_rank = block_excl_sum(n_eq, scratch, tot);
-    bool sel[KPT];
-    int n_sel = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const bool is_eq = valid[j] && key[j] == v;
-        sel[j] = (valid[j] && key[j] > v) || (is_eq && eq_rank < need_eq);
-        eq_rank += is_eq ? 1 : 0;
-        n_sel += sel[j] ? 1 : 0;
-    }
-    int pos = block_excl_sum(n_sel, scratch, tot);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        if (!valid[j]) continue;
-        if (sel[j] && pos < C) {
-            idx[(int64_t)e * C + pos] = tb + j;
-            wt[(int64_t)e * C + pos] = pv[j];
+        for (int c = 0; c < 4; ++c) {
+            n_eq += key[j][c] == v ? 1 : 0;
+            n_gt += key[j][c] > v ? 1 : 0;
         }
-        if (slotmap) slotmap[(int64_t)e * T + tb + j] = sel[j] ? pos : -1;
-        pos += sel[j] ? 1 : 0;
+    n_eq = (int)wave_reduce_u32((uint32_t)n_eq, uadd2);
+    n_gt = (int)wave_reduce_u32((uint32_t)n_gt, uadd2);
+    if (lane == 0) {
+        s_cnt[w] = n_eq;
+        s_cnt[kSelV + w] = n_gt;
+    }
+    __syncthreads();
+    int eqb = 0, gtb = 0;
+#pragma unroll
+    for (int x = 0; x < kSelV; ++x) {
+        eqb += x < w ? s_cnt[x] : 0;
+        gtb += x < w ? s_cnt[kSelV + x] : 0;
+    }
+    int32_t* sm = slotmap ? slotmap + (int64_t)e * T : nullptr;
+    const bool vec_sm = vec && sm && (reinterpret_cast<uintptr_t>(sm) & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+        const int t = tb + 256 * j;
+        bool eq[4], gt[4];
+        int ne = 0, ng = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            eq[c] = key[j][c] == v;
+            gt[c] = key[j][c] > v;
+            ne += eq[c] ? 1 : 0;
+            ng += gt[c] ? 1 : 0;
+        }
+        int tot_eq, tot_gt;
+        int eqr = eqb + lanes_below(ne, tot_eq);
+        int gtr = gtb + lanes_below(ng, tot_gt);
+        int slot[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool sel = gt[c] || (eq[c] && eqr < need_eq);
+            const int pos = gtr + (eqr < need_eq ? eqr : need_eq);
+            slot[c] = sel ? pos : -1;
+            if (sel && pos < C) {
+                idx[(int64_t)e * C + pos] = t + c;
+                float v_out;
+                if constexpr (kKeepVal) {
+                    v_out = val[j][c];
+                } else {
+                    const uint32_t k = key[j][c];
+                    v_out = k == 0x80000000u ? p[t + c] : __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+                }
+                wt[(int64_t)e * C + pos] = v_out;
+            }
+            eqr += eq[c] ? 1 : 0;
+            gtr += gt[c] ? 1 : 0;
+        }
+        if (sm) {
+            if (vec_sm && t < T) {
+                *reinterpret_cast<int4*>(sm + t) = make_int4(slot[0], slot[1], slot[2], slot[3]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (t + c < T) sm[t + c] = slot[c];
+            }
+        }
+        eqb += tot_eq;
+        gtb += tot_gt;
     }
 }
 
@@ -378,11 +519,10 @@ hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* 
 
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
                               int32_t* slotmap, hipStream_t st) {
-    const dim3 grid(E), block(kSelThreads);
-#define CRK_SEL(K)                                                                            \
-    if (T <= kSelThreads * K) {                                                               \
-        select_topc_reg_kernel<K><<<grid, block, 0, st>>>(probs_t, T, C, idx, wt, slotmap);   \
-        return hipGetLastError();                                                             \
+#define CRK_SEL(K)                                                                                      \
+    if (T <= kSelV * 256 * K) {                                                                         \
+        select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slotmap); \
+        return hipGetLastError();                                                                       \
     }
     CRK_SEL(1)
     CRK_SEL(2)
@@ -390,7 +530,7 @@ hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t
     CRK_SEL(8)
     CRK_SEL(16)
 #undef CRK_SEL
-    select_topc_kernel<<<grid, block, 0, st>>>(probs_t, T, C, idx, wt, slotmap);
+    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap);
     return hipGetLastError();
 }
 
