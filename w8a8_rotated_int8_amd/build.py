@@ -19,7 +19,9 @@ FLAGS = [
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"),
+    "-I" + BUILD,
 ]
+CC = os.environ.get("CC", "gcc")
 
 
 def _compile(src: str) -> str:
@@ -32,9 +34,29 @@ def _compile(src: str) -> str:
     return obj
 
 
+def silu_table(kind: str = "inc") -> str:
+    """Build and run the host generator of the SwiGLU gate activation table (every bf16 input); returns the
+    path of its output (`inc`: C initializer included by gemm.hip, `bin`: 65536 little-endian floats)."""
+    os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "silu_table_gen")
+    src = os.path.join(CSRC, "silu_table_gen.c")
+    r = subprocess.run([CC, "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", src, "-o", exe, "-lm"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"silu table generator failed to build:\n{r.stdout}\n{r.stderr}")
+    out = os.path.join(BUILD, "silu_table." + kind)
+    with open(out + ".tmp", "wb") as fh:
+        r = subprocess.run([exe, kind], stdout=fh, stderr=subprocess.PIPE)
+    if r.returncode != 0:
+        raise RuntimeError(f"silu table generator failed:\n{r.stderr.decode()}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    silu_table("inc")
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()

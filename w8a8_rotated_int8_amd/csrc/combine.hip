@@ -3,21 +3,26 @@
 //
 // out[t, :] = bf16( sum over experts e in ascending order that took t of w[e, c] * z[e*C + c, :] ), fp32,
 // starting from +0.0f, one rounding at the end; tokens taken by no expert get +0.  Deterministic: one
-// workgroup per token, no atomics, so the sum order is fixed.
+// wavefront per token, no atomics, so the sum order is fixed.
 //
-// Each wave reads the slot map entries of up to 64 experts in one vector load (lane = expert), ballots the
-// experts that took the token, and walks that mask from the lowest expert up.
+// One wavefront per token.  Lane e reads the slot map entry of expert e (up to 64 at a time), a ballot gives
+// the experts that took the token, and their rows are summed from the lowest expert up.  The row loads of
+// up to kBatch experts are all issued before any of them is summed, so a token costs one memory latency per
+// kBatch experts rather than one per expert.  Lane l owns the 16-byte chunks l, l + 64, ... of the row.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace crk {
 namespace {
 
-template <int CH>  // 16-byte chunks (8 bf16) per thread
+constexpr int kBatch = 4;
+
+template <int CH>  // 16-byte chunks (8 bf16) per lane
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ z, const int32_t* __restrict__ slotmap,
                                                       const float* __restrict__ wt, int T, int E, int C, int d,
                                                       uint16_t* __restrict__ out) {
-    const int t = blockIdx.x;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // wave-uniform
     const int lane = threadIdx.x & 63;
     const int nch = d >> 3;
     float acc[CH][8];
@@ -32,25 +37,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         const float w = (c >= 0) ? wt[(int64_t)e * C + c] : 0.0f;
         uint64_t taken = __ballot(c >= 0);
         while (taken) {
-            const int l = __ffsll((unsigned long long)taken) - 1;
-            taken &= taken - 1;
-            const int cs = __shfl(c, l);
-            const float ws = __shfl(w, l);
-            const uint16_t* zr = z + ((int64_t)(e0 + l) * C + cs) * d;
+            // the next (up to) kBatch experts, lowest first
+            int cnt = 0;
+            uint4 raw[kBatch][CH];
+            float wb[kBatch];
 #pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const int ch = threadIdx.x + 256 * j;
-                if (ch < nch) {
-                    const uint4 raw = *reinterpret_cast<const uint4*>(zr + 8 * ch);
-                    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+            for (int b = 0; b < kBatch; ++b) {
+                if (taken) {
+                    const int l = __ffsll((unsigned long long)taken) - 1;
+                    taken &= taken - 1;
+                    const int cs = __builtin_amdgcn_readlane(c, l);
+                    wb[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), l));
+                    const uint16_t* zr = z + ((int64_t)(e0 + l) * C + cs) * d;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float z0 = bf16_to_float(wv[q] & 0xffffu);
-                        const float z1 = bf16_to_float(wv[q] >> 16);
-                        const float p0 = ws * z0;
-                        const float p1 = ws * z1;
-                        acc[j][2 * q] = acc[j][2 * q] + p0;
-                        acc[j][2 * q + 1] = acc[j][2 * q + 1] + p1;
+                    for (int j = 0; j < CH; ++j) {
+                        const int ch = lane + 64 * j;
+                        raw[b][j] = ch < nch ? *reinterpret_cast<const uint4*>(zr + 8 * ch) : make_uint4(0u, 0u, 0u, 0u);
+                    }
+                    cnt = b + 1;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (b < cnt) {
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const uint32_t wv[4] = {raw[b][j].x, raw[b][j].y, raw[b][j].z, raw[b][j].w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float z0 = bf16_to_float(wv[q] & 0xffffu);
+                            const float z1 = __uint_as_float(wv[q] & 0xffff0000u);
+                            const float p0 = wb[b] * z0;
+                            const float p1 = wb[b] * z1;
+                            acc[j][2 * q] = acc[j][2 * q] + p0;
+                            acc[j][2 * q + 1] = acc[j][2 * q + 1] + p1;
+                        }
                     }
                 }
             }
@@ -58,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int ch = threadIdx.x + 256 * j;
+        const int ch = lane + 64 * j;
         if (ch < nch) {
             uint4 o;
             o.x = float_to_bf16(acc[j][0]) | (float_to_bf16(acc[j][1]) << 16);
@@ -75,11 +96,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const float* wt, int T, int E, int C, int d,
                           uint16_t* out, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const int ch = (d / 8 + 255) / 256;
-    const dim3 grid(T), block(256);
+    const int ch = (d / 8 + 63) / 64;
+    const dim3 grid((T + 3) / 4), block(256);
     if (ch <= 1) combine_kernel<1><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
     else if (ch <= 2) combine_kernel<2><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
     else if (ch <= 4) combine_kernel<4><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
+    else if (ch <= 8) combine_kernel<8><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
+    else if (ch <= 16) combine_kernel<16><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

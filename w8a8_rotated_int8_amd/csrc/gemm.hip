@@ -61,6 +61,16 @@ constexpr int kOobOffset = 0x40000000;    // byte offset past every output range
 // Cache policy of the weight DMAs: non-temporal; streaming with nt measured ~6.5 TB/s vs ~5.7 TB/s without.
 constexpr int kNonTemporal = 2;
 
+// SwiGLU gate activation silu(g) = g / (1 + E(-g)) for every bf16 bit pattern g (index = the bits), built on
+// the host from the same definition.  The epilogue keeps the window of gate values with |g| in [2^-13, 2^5)
+// (bf16 exponent fields 114..131, both signs: 4608 entries, 18 KiB) in LDS and evaluates E for the rest.
+__device__ const uint32_t kSiluTable[65536] = {
+#include "silu_table.inc"
+};
+constexpr uint32_t kSiluLo = 114u << 7;       // first (sign-less) bf16 pattern of the window
+constexpr uint32_t kSiluSpan = 18u << 7;      // patterns per sign
+constexpr int kSiluBytes = 2 * kSiluSpan * 4;
+
 // Sign-extend the 8 nibbles of w (code 2j in the low nibble of byte j) into 8 int8 bytes, in k order.
 __device__ __forceinline__ uint2 unpack_nibbles(uint32_t w) {
     uint32_t lo = w & 0x0f0f0f0fu;
@@ -124,7 +134,8 @@ struct GemmCfg {
     static constexpr int CSC_OFF = B_RING + A_RING;           // NSC slots of 256 column scales
     static constexpr int SROW_OFF = CSC_OFF + NSC * kBN * 4;  // NSC slots of BM row scales
     static constexpr int ROWS_OFF = SROW_OFF + NSC * BM * 4;  // 2 slots of BM gathered row indices
-    static constexpr int LDS = ROWS_OFF + 2 * BM * 4;
+    static constexpr int SILU_OFF = ROWS_OFF + 2 * BM * 4;   // SwiGLU: the gate activation window
+    static constexpr int LDS = SILU_OFF + (EPI == Epi::kSwiGLU ? kSiluBytes : 0);
     static_assert(BM == 64 || BM == 128 || BM == 256, "tile rows");
     static_assert(NAW >= 1 && NAW * 4096 == A_BYTES, "activation stage / loader mismatch");
     static_assert(SB >= 3 && SA >= 3, "ring depth");
@@ -146,6 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     float* const csc_lds = reinterpret_cast<float*>(smem + Cfg::CSC_OFF);
     float* const srow_lds = reinterpret_cast<float*>(smem + Cfg::SROW_OFF);
     int32_t* const rows_lds = reinterpret_cast<int32_t*>(smem + Cfg::ROWS_OFF);
+    float* const silu_lds = reinterpret_cast<float*>(smem + Cfg::SILU_OFF);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -484,21 +496,34 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 for (int tm = 0; tm < TM; ++tm) {
                     const float sx = srow[tm * 32 + (lane & 31)];
                     const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
+                    // gate and up rounded to bf16 in one conversion; the gate's bits index the activation table
+                    uint32_t gu[16];
+                    float sg[16];
+                    bool out_of_window = false;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float gt = (float)acc[tm][0][r];
+                        gt = gt * sx;
+                        gt = gt * cg[r];
+                        float up = (float)acc[tm][1][r];
+                        up = up * sx;
+                        up = up * cu[r];
+                        gu[r] = pack_bf16x2(gt, up);
+                        const uint32_t off = (gu[r] & 0x7fffu) - kSiluLo;
+                        const bool in = off < kSiluSpan;
+                        out_of_window |= !in;
+                        sg[r] = silu_lds[in ? off + ((gu[r] >> 15) & 1u) * kSiluSpan : 0u];
+                    }
+                    if (__builtin_expect(__ballot(out_of_window) != 0, 0)) {  // wave-uniform
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if ((gu[r] & 0x7fffu) - kSiluLo >= kSiluSpan) sg[r] = silu_fixed(__uint_as_float(gu[r] << 16));
+                    }
                     float a[4][4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            float gt = (float)acc[tm][0][4 * j + x];
-                            gt = gt * sx;
-                            gt = gt * cg[4 * j + x];
-                            float up = (float)acc[tm][1][4 * j + x];
-                            up = up * sx;
-                            up = up * cu[4 * j + x];
-                            const float gb = bf16_to_float(float_to_bf16(gt));
-                            const float ub = bf16_to_float(float_to_bf16(up));
-                            a[j][x] = silu_fixed(gb) * ub;
-                        }
+                        for (int x = 0; x < 4; ++x) a[j][x] = sg[4 * j + x] * __uint_as_float(gu[4 * j + x] & 0xffff0000u);
                     store_pair(row, col0, 0, 1, a[0], a[1]);
                     store_pair(row, col0, 2, 3, a[2], a[3]);
                 }
@@ -534,6 +559,14 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         else
             wait_vmcnt_dyn(x);
     };
+
+    if constexpr (EPI == Epi::kSwiGLU) {
+        // the activation window, published by the prologue's barrier
+        for (int k = tid; k < (int)(2 * kSiluSpan); k += kThreads) {
+            const uint32_t pat = (k < (int)kSiluSpan ? 0u : 0x8000u) + kSiluLo + (uint32_t)(k % (int)kSiluSpan);
+            silu_lds[k] = __uint_as_float(kSiluTable[pat]);
+        }
+    }
 
     // prologue: every ring slot takes a stage; hist[t] = operations issued up to the end of stage t
 #pragma unroll
@@ -625,14 +658,16 @@ template <Epi EPI, int WBITS, bool TILED>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
     // Weight ring depth: what the LDS leaves after the 3-stage activation ring; 4-bit weight stages are half
     // the size, so about twice as many.
+    // SwiGLU gives 18 KiB of LDS to the activation window, so its weight rings are shorter.
+    constexpr bool kSw = EPI == Epi::kSwiGLU;
     if constexpr (WBITS == 8) {
-        if (p.M <= 64) return launch_cfg<64, 8, 3, EPI, WBITS, TILED>(p, st);
-        if (p.M <= 128) return launch_cfg<128, 7, 3, EPI, WBITS, TILED>(p, st);
-        return launch_cfg<256, 6, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 64) return launch_cfg<64, kSw ? 7 : 8, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 128) return launch_cfg<128, kSw ? 6 : 7, 3, EPI, WBITS, TILED>(p, st);
+        return launch_cfg<256, kSw ? 5 : 6, 3, EPI, WBITS, TILED>(p, st);
     } else {
-        if (p.M <= 64) return launch_cfg<64, 14, 3, EPI, WBITS, TILED>(p, st);
-        if (p.M <= 128) return launch_cfg<128, 13, 3, EPI, WBITS, TILED>(p, st);
-        return launch_cfg<256, 10, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 64) return launch_cfg<64, kSw ? 12 : 14, 3, EPI, WBITS, TILED>(p, st);
+        if (p.M <= 128) return launch_cfg<128, kSw ? 11 : 13, 3, EPI, WBITS, TILED>(p, st);
+        return launch_cfg<256, kSw ? 8 : 10, 3, EPI, WBITS, TILED>(p, st);
     }
 }
 
