@@ -82,10 +82,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         const int ch = lane + 64 * j;
         if (ch < nch) {
             uint4 o;
-            o.x = float_to_bf16(acc[j][0]) | (float_to_bf16(acc[j][1]) << 16);
-            o.y = float_to_bf16(acc[j][2]) | (float_to_bf16(acc[j][3]) << 16);
-            o.z = float_to_bf16(acc[j][4]) | (float_to_bf16(acc[j][5]) << 16);
-            o.w = float_to_bf16(acc[j][6]) | (float_to_bf16(acc[j][7]) << 16);
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
             *reinterpret_cast<uint4*>(out + (int64_t)t * d + 8 * ch) = o;
         }
     }

@@ -20,6 +20,13 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two fp32 values -> packed bf16 (lo in bits 0-15), same rounding, one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // The library's fixed fp32 exponential E(x).  The argument is clamped to [-86, 88]; then Cody-Waite
 // reduction x = n ln2 + r with ln2 split into a 16-significant-bit head (n * head exact for |n| < 256) and an
 // fp32 tail (one fused multiply-add each), e^r from the Taylor series through r^7 (coefficients 1/k! rounded to

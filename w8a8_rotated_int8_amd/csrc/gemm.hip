@@ -95,9 +95,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return float_to_bf16(lo) | (float_to_bf16(hi) << 16);
-}
 
 // vmcnt(x) for a wave-uniform x (binary search over the immediate forms; scalar branches only).
 template <int L, int H>
@@ -427,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 for (int r = 0; r < 16; ++r) {
                     int n = wblk(blk, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                     n = n < N ? n : N - 1;
-                    b[r] = p.bias ? bf16_to_float(p.bias[n]) : 0.0f;
+                    b[r] = bf16_to_float(p.bias[n]);
                 }
             };
             // Two runs j0 < j1 of 4 outputs each, per lane: lanes l and l + 32 hold the two halves of an 8-column
@@ -464,27 +461,35 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 // weight block outer, so only one block's scales and bias are live
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    float cs[16], bias[16];
+                    float cs[16];
                     load_cs(q, cs);
-                    load_bias(q, bias);
                     const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 4 * h;
+                    auto rows_out = [&](bool with_bias, const float (&bias)[16]) {
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm) {
-                        const float sx = srow[tm * 32 + (lane & 31)];
-                        const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
-                        float v[4][4];
+                        for (int tm = 0; tm < TM; ++tm) {
+                            const float sx = srow[tm * 32 + (lane & 31)];
+                            const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
+                            float v[4][4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
+                            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                            for (int x = 0; x < 4; ++x) {
-                                float t = (float)acc[tm][q][4 * j + x];
-                                t = t * sx;
-                                t = t * cs[4 * j + x];
-                                if (p.bias) t = t + bias[4 * j + x];
-                                v[j][x] = t;
-                            }
-                        store_pair(row, col0, 0, 1, v[0], v[1]);
-                        store_pair(row, col0, 2, 3, v[2], v[3]);
+                                for (int x = 0; x < 4; ++x) {
+                                    float t = (float)acc[tm][q][4 * j + x];
+                                    t = t * sx;
+                                    t = t * cs[4 * j + x];
+                                    if (with_bias) t = t + bias[4 * j + x];
+                                    v[j][x] = t;
+                                }
+                            store_pair(row, col0, 0, 1, v[0], v[1]);
+                            store_pair(row, col0, 2, 3, v[2], v[3]);
+                        }
+                    };
+                    if (p.bias) {  // uniform: one copy of the loop per case
+                        float bias[16];
+                        load_bias(q, bias);
+                        rows_out(true, bias);
+                    } else {
+                        rows_out(false, cs);
                     }
                 }
             } else {
