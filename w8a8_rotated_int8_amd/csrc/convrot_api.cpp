@@ -5,7 +5,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <mutex>
 #include <vector>
 
 #include "../../include/convrot.h"
@@ -132,36 +131,6 @@ crk::GemmProblem down_problem(const int8_t* qa, const float* sa, int C, const co
     return p;
 }
 
-// The forward's second stream: the token rotate+quantise does not depend on the routing, so it runs beside
-// softmax and top-C selection (whose 64 selection workgroups leave most CUs idle) and is joined back with an
-// event before the gate/up GEMM.  One stream and two events per device, created on first use at the default
-// priority and kept until the process ends; `lock` keeps the record/wait pairs of concurrent host callers
-// from interleaving.
-struct SideStream {
-    std::mutex lock;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool ready = false, failed = false;
-};
-
-SideStream* side_stream() {
-    constexpr int kMaxDev = 64;
-    static SideStream side[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
-    SideStream& ss = side[dev];
-    std::lock_guard<std::mutex> g(ss.lock);
-    if (!ss.ready && !ss.failed) {
-        if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess)
-            ss.ready = true;
-        else
-            ss.failed = true;  // the forward then runs every step on the caller's stream
-    }
-    return ss.ready ? &ss : nullptr;
-}
-
 #define CRK_TRY(expr)                                   \
     do {                                                \
         const hipError_t crk_e_ = (expr);               \
@@ -281,21 +250,16 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
     float* wt = wt_out ? wt_out : b.wt;
     const int64_t S = (int64_t)w->E * C;
 
-    SideStream* ss = side_stream();
-    if (ss) {
-        std::lock_guard<std::mutex> g(ss->lock);
-        CRK_TRY(hipEventRecord(ss->fork, stream));
-        CRK_TRY(hipStreamWaitEvent(ss->stream, ss->fork, 0));
-        CRK_TRY(crk::launch_rotq_act(x, T, w->d, w->group_gu, b.qx, b.sx, nullptr, ss->stream));
-        CRK_TRY(hipEventRecord(ss->join, ss->stream));
+    // softmax and the token rotate+quantise share one launch where the shapes allow (they are independent)
+    const hipError_t fused =
+        crk::launch_softmax_rotq(router_logits, T, w->E, b.probs_t, x, w->d, w->group_gu, b.qx, b.sx, stream);
+    if (fused == hipErrorNotSupported) {
         CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w->E, b.probs_t, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
-        CRK_TRY(hipStreamWaitEvent(stream, ss->join, 0));
-    } else {
-        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w->E, b.probs_t, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
         CRK_TRY(crk::launch_rotq_act(x, T, w->d, w->group_gu, b.qx, b.sx, nullptr, stream));
+    } else {
+        CRK_TRY(fused);
     }
+    CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
     CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, *w, b.a), stream));
     CRK_TRY(crk::launch_rotq_act(b.a, S, w->I, w->group_dn, b.qa, b.sa, nullptr, stream));
     CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, *w, b.z), stream));

@@ -23,6 +23,10 @@ hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* 
                             hipStream_t st);
 // Per expert: top-C selection on probs_t[e, :]; writes idx [E, C], wt [E, C] and, if slotmap != nullptr,
 // slotmap [E, T] (position of token t in expert e's list, or -1).
+// Router softmax (E <= 64, logits) and token rotate+quantise (fast shapes) in one launch; returns
+// hipErrorNotSupported, having launched nothing, for other shapes.
+hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, const uint16_t* x, int K,
+                               int group, int8_t* qx, float* sx, hipStream_t st);
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
                               int32_t* slotmap, hipStream_t st);
 // slotmap [E, T] from idx [E, C].

@@ -13,6 +13,7 @@
 // plain loop.  The row maximum is a wave reduction, the codes use IEEE division and rint.
 #include "device_common.h"
 #include "kernels.h"
+#include "rotq_fast.h"
 
 namespace crk {
 namespace {
@@ -201,137 +202,12 @@ __global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__
     if (lane == 0 && !pad) sout[row] = scale;
 }
 
-// ---- activation rows, fast path: K a multiple of 8 g ------------------------------------------------------
-// Lane l holds, in each of R = K / (8 g) rounds, the contiguous run of E = g / 8 elements
-// [round * 8g + l * E, + E): every g-block sits on 8 consecutive lanes, so the transform runs its stages
-// h < E inside the lane and only h = E, 2E, 4E across lanes (partner lane l ^ 1, ^ 2 via DPP quad
-// permutations, ^ 4 via a swizzle).  Every stage still forms the pairs (a + b, a - b) of the ascending-h
-// transform, so the fp32 values are those of the plain loop.
-//
-// Quantiser division: with y = 1 / scale rounded to nearest (one IEEE division per row), the quotient
-// q0 = r y, its exact remainder e = fma(-q0, scale, r) and q = fma(e, y, q0) give the correctly rounded
-// r / scale (Markstein's theorem; it needs the remainder to be exact, which holds while scale >= 2^-96 --
-// checked exhaustively on random and half-integer quotients over the whole fp32 range).  Smaller scales
-// take the IEEE division.
-
-__device__ __forceinline__ float dpp_xor1(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
-}
-__device__ __forceinline__ float swz_xor4(float v) {
-    // ds_swizzle bit-mask mode: and 0x1f, or 0, xor 4 (within 32 lanes)
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
-}
-
-// Code byte of a quotient t with |t| <= 127.5: clamp to [-127, 127], then adding 1.5 * 2^23 rounds to the
-// nearest integer (ties to even, as rint) and leaves it in the low mantissa bits, whose low byte is the code
-// in two's complement.
-__device__ __forceinline__ uint32_t code_bits(float t) {
-    return __float_as_uint(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f) + 12582912.0f);
-}
-// Low bytes of four such words, packed in order.
-__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // bytes: a0, b0, 0, 0
-    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // bytes: 0, 0, c0, d0
-    return ab | cd;
-}
-
 template <int G, int R>
 __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __restrict__ x, int64_t rows, int K,
                                                             int8_t* __restrict__ q, float* __restrict__ s) {
-    constexpr int E = G / 8;  // elements per lane per round
-    const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // wave-uniform
-    const uint16_t* src = x + row * (int64_t)K + lane * E;
-    float v[R][E];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < E / 8; ++c) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c);
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[r][8 * c + 2 * e] = bf16_to_float(w[e] & 0xffffu);
-                v[r][8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-            }
-        }
-    constexpr float kNorm = (G == 256) ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
-    // Across lanes the pair (a + b, a - b) is other + sgn * mine: the lower lane of a pair adds, the upper
-    // lane subtracts its own value from its partner's (multiplying by +-1 is exact, the fma rounds once).
-    const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f, sg4 = (lane & 4) ? -1.0f : 1.0f;
-    float amax = 0.0f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int h = 1; h < E; h *= 2)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                if ((e & h) == 0) {
-                    const float a = v[r][e], b = v[r][e + h];
-                    v[r][e] = a + b;
-                    v[r][e + h] = a - b;
-                }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float mine = v[r][e];
-            mine = __builtin_fmaf(sg1, mine, dpp_xor1(mine));
-            mine = __builtin_fmaf(sg2, mine, dpp_xor2(mine));
-            mine = __builtin_fmaf(sg4, mine, swz_xor4(mine));
-            mine = mine * kNorm;
-            v[r][e] = mine;
-            amax = fmaxf(amax, fabsf(mine));
-        }
-    }
-    amax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(amax))));  // wave-uniform
-    const float scale = amax / 127.0f;
-    int8_t* dst = q + row * (int64_t)K + lane * E;
-    auto store_round = [&](int r, const uint32_t (&packed)[E / 4]) {
-        if constexpr (E == 8) {
-            *reinterpret_cast<uint2*>(dst + r * 8 * G) = make_uint2(packed[0], packed[1]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < E / 16; ++c)
-                *reinterpret_cast<uint4*>(dst + r * 8 * G + 16 * c) =
-                    make_uint4(packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]);
-        }
-    };
-    if (scale >= 0x1p-96f) {
-        const float y = 1.0f / scale;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t packed[E / 4];
-#pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                uint32_t b[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float q0 = v[r][e + u] * y;
-                    const float rem = __builtin_fmaf(-q0, scale, v[r][e + u]);
-                    b[u] = code_bits(__builtin_fmaf(rem, y, q0));
-                }
-                packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
-            }
-            store_round(r, packed);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t packed[E / 4];
-#pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                uint32_t b[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) b[u] = code_bits(scale == 0.0f ? 0.0f : v[r][e + u] / scale);
-                packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
-            }
-            store_round(r, packed);
-        }
-    }
-    if (lane == 0) s[row] = scale;
+    rotq_fast_row<G, R>(x, row, K, q, s);
 }
 
 // rows: source rows (E * N for weights); N: rows per expert (tiled modes only).

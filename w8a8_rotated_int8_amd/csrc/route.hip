@@ -14,6 +14,7 @@
 //  build_slotmap per expert: slotmap[e, t] = position of t in expert e's list, or -1.
 #include "device_common.h"
 #include "kernels.h"
+#include "rotq_fast.h"
 
 namespace crk {
 namespace {
@@ -32,12 +33,13 @@ constexpr int kSmTok = 32;
 constexpr int kSmStride = 65;           // LDS row stride of the [token][expert] tile (floats)
 constexpr int kSmTrStride = kSmTok + 1;  // LDS row stride of the [expert][token] tile
 
-__global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
-                                                              float* __restrict__ probs_t, float* __restrict__ probs_out) {
+// Tokens [32 b, 32 b + 32) (one 256-thread workgroup).
+__device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int is_probs, int T, int E,
+                                             float* __restrict__ probs_t, float* __restrict__ probs_out, int b) {
     __shared__ float tile[kSmTok * kSmStride];  // logits, then exponentials
     __shared__ float tr[64 * kSmTrStride];      // probabilities, transposed
     __shared__ float zrow[kSmTok];
-    const int t0 = blockIdx.x * kSmTok;
+    const int t0 = b * kSmTok;
     const int ntok = (T - t0) < kSmTok ? (T - t0) : kSmTok;
     const int tid = threadIdx.x, tok = tid >> 3, eg = tid & 7;
     const float* src = in + (int64_t)t0 * E;
@@ -116,6 +118,28 @@ __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __res
             if (c < ntok) probs_t[(int64_t)e * T + t0 + c] = tr[e * kSmTrStride + c];
         }
     }
+}
+
+__global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
+                                                              float* __restrict__ probs_t, float* __restrict__ probs_out) {
+    softmax_tile(in, is_probs, T, E, probs_t, probs_out, blockIdx.x);
+}
+
+// The router softmax and the token rotate+quantise in one launch: they do not depend on each other, so the
+// first nsm workgroups take softmax tiles and the rest take four token rows each; the rotate+quantise
+// workgroups fill the CUs the short softmax leaves idle, with no second stream to join.
+template <int G, int R>
+__global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restrict__ logits, int T, int E,
+                                                           float* __restrict__ probs_t, int nsm,
+                                                           const uint16_t* __restrict__ x, int K,
+                                                           int8_t* __restrict__ qx, float* __restrict__ sx) {
+    if ((int)blockIdx.x < nsm) {  // workgroup-uniform
+        softmax_tile(logits, 0, T, E, probs_t, nullptr, blockIdx.x);
+        return;
+    }
+    const int64_t row = (int64_t)(blockIdx.x - nsm) * 4 + (threadIdx.x >> 6);
+    if (row >= T) return;  // wave-uniform
+    rotq_fast_row<G, R>(x, row, K, qx, sx);
 }
 
 // ---- softmax, any E (one thread per token) ------------------------------------------------------------
@@ -515,6 +539,29 @@ hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* 
     else
         softmax_t_kernel<<<dim3((T + 255) / 256), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t, probs_out);
     return hipGetLastError();
+}
+
+hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, const uint16_t* x, int K,
+                               int group, int8_t* qx, float* sx, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (E > 64 || K % (8 * group) != 0) return hipErrorNotSupported;
+    const int nsm = (T + kSmTok - 1) / kSmTok;
+    const int64_t nrot = ((int64_t)T + 3) / 4;
+    const dim3 grid((unsigned)(nsm + nrot)), block(256);
+    const int R = K / (8 * group);
+#define CRK_SR(GG, RR)                                                                                  \
+    if (group == GG && R == RR) {                                                                       \
+        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, nsm, x, K, qx, sx);   \
+        return hipGetLastError();                                                                       \
+    }
+    CRK_SR(256, 1)
+    CRK_SR(256, 2)
+    CRK_SR(256, 4)
+    CRK_SR(64, 1)
+    CRK_SR(64, 2)
+    CRK_SR(64, 4)
+#undef CRK_SR
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
