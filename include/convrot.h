@@ -80,7 +80,9 @@ const char* convrot_status_str(convrot_status s);
  *    coalesced 16-byte load per lane.  With r = n % 32:
  *      int8 (K-blocks of 32):  byte ((nb*(K/32) + k/32)*1024 + (r + 32*((k%32)/16))*16 + k%16)
  *      int4 (K-blocks of 64):  byte ((nb*(K/64) + k/64)*1024 + (r + 32*((k%32)/16))*16 + 8*((k%64)/32)
- *                                    + (k%16)/2), nibble k%2 (even k in bits 0-3); requires K % 64 == 0.
+ *                                    + 4*((k%16)/8) + k%4), low nibble if k%8 < 4, else high nibble (each
+ *                                    4-byte word: k..k+3 in the low nibbles, k+4..k+7 in the high ones);
+ *                                    requires K % 64 == 0.
  *    For [E, N, K] weights expert e starts at byte e * NB * K (int8) or e * NB * K / 2 (int4), i.e. the
  *    buffer holds E * NB * 32 * K (or half that) bytes. */
 typedef enum convrot_layout { CONVROT_LAYOUT_ROWMAJOR = 0, CONVROT_LAYOUT_MFMA = 1 } convrot_layout;

@@ -71,15 +71,14 @@ constexpr uint32_t kSiluLo = 114u << 7;       // first (sign-less) bf16 pattern 
 constexpr uint32_t kSiluSpan = 18u << 7;      // patterns per sign
 constexpr int kSiluBytes = 2 * kSiluSpan * 4;
 
-// Sign-extend the 8 nibbles of w (code 2j in the low nibble of byte j) into 8 int8 bytes, in k order.
+// Sign-extend the 8 nibbles of a tiled int4 word into 8 int8 bytes in k order: the low nibbles hold the first
+// 4 k, the high nibbles the next 4.  Per byte, n ^ 0x88 = 0x80 + (v + 8) for the 4-bit two's complement v;
+// subtracting 8 cannot borrow out of the byte, and xor 0x80 leaves v as an int8.
 __device__ __forceinline__ uint2 unpack_nibbles(uint32_t w) {
-    uint32_t lo = w & 0x0f0f0f0fu;
-    uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
-    lo |= (lo & 0x08080808u) * 0x1eu;  // 0x08 * 0x1e = 0xf0 per byte: fills the upper nibble with the sign
-    hi |= (hi & 0x08080808u) * 0x1eu;
+    const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
     uint2 r;
-    r.x = (lo & 0xffu) | ((hi & 0xffu) << 8) | ((lo & 0xff00u) << 8) | ((hi & 0xff00u) << 16);
-    r.y = ((lo >> 16) & 0xffu) | ((hi >> 8) & 0xff00u) | ((lo >> 8) & 0xff0000u) | (hi & 0xff000000u);
+    r.x = ((lo ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
+    r.y = ((hi ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
     return r;
 }
 

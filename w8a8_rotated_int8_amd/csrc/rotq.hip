@@ -176,9 +176,12 @@ __global__ __launch_bounds__(256) void rotq_rows_kernel(const void* __restrict__
             for (int e = 0; e < 8; ++e) c[e] = quant_code<QMAX>(x[j].v[e], scale);
         }
         if constexpr (OUT == Out::kRowI4 || OUT == Out::kTiledI4) {
+            // row-major: code e in nibble e (even k low); tiled: codes 0-3 in the low nibbles of bytes 0-3 and
+            // codes 4-7 in their high nibbles, so the GEMM widens a word with two masks
             uint32_t packed = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) packed |= (uint32_t)(c[e] & 0xf) << (4 * e);
+            for (int e = 0; e < 8; ++e)
+                packed |= (uint32_t)(c[e] & 0xf) << (OUT == Out::kTiledI4 ? 8 * (e & 3) + 4 * (e >> 2) : 4 * e);
             const int64_t off = (OUT == Out::kRowI4)
                                     ? row * (int64_t)(K / 2) + 4 * i
                                     : expert * (int64_t)(((N + 31) >> 5) << 5) * (K / 2) + tiled_offset<true>(n, 8 * i, K);
