@@ -504,6 +504,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                     uint32_t gu[16];
                     float sg[16];
                     bool out_of_window = false;
+                    // window entry 2 (m - kSiluLo) + sign holds the gate with magnitude pattern m
+                    const float* const silu_win = silu_lds - 2 * kSiluLo;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float gt = (float)acc[tm][0][r];
@@ -513,10 +515,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                         up = up * sx;
                         up = up * cu[r];
                         gu[r] = pack_bf16x2(gt, up);
-                        const uint32_t off = (gu[r] & 0x7fffu) - kSiluLo;
-                        const bool in = off < kSiluSpan;
-                        out_of_window |= !in;
-                        sg[r] = silu_lds[in ? off + ((gu[r] >> 15) & 1u) * kSiluSpan : 0u];
+                        // magnitude pattern clamped into the window (one med3); a clamped value is out of it
+                        const uint32_t mag = gu[r] & 0x7fffu;
+                        const uint32_t mc = min(max(mag, kSiluLo), kSiluLo + kSiluSpan - 1u);
+                        out_of_window |= mag != mc;
+                        const uint32_t sgn = __builtin_amdgcn_ubfe(gu[r], 15, 1);
+                        sg[r] = silu_win[(mc << 1) + sgn];
                     }
                     if (__builtin_expect(__ballot(out_of_window) != 0, 0)) {  // wave-uniform
 #pragma unroll
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     if constexpr (EPI == Epi::kSwiGLU) {
         // the activation window, published by the prologue's barrier
         for (int k = tid; k < (int)(2 * kSiluSpan); k += kThreads) {
-            const uint32_t pat = (k < (int)kSiluSpan ? 0u : 0x8000u) + kSiluLo + (uint32_t)(k % (int)kSiluSpan);
+            const uint32_t pat = (k & 1 ? 0x8000u : 0u) + kSiluLo + (uint32_t)(k >> 1);
             silu_lds[k] = __uint_as_float(kSiluTable[pat]);
         }
     }
