@@ -2,13 +2,15 @@
 // "Conversion notes": each expert picks its top-C tokens and the results are scattered back).
 //
 // out[t, :] = bf16( sum over experts e in ascending order that took t of w[e, c] * z[e*C + c, :] ), fp32,
-// starting from +0.0f, one rounding at the end; tokens taken by no expert get +0.  Deterministic: one
-// wavefront per token, no atomics, so the sum order is fixed.
+// starting from +0.0f, one rounding at the end; tokens taken by no expert get +0.  Deterministic: every output
+// element is summed by one lane, no atomics, so the sum order is fixed.
 //
-// One wavefront per token.  Lane e reads the slot map entry of expert e (up to 64 at a time), a ballot gives
-// the experts that took the token, and their rows are summed from the lowest expert up.  The row loads of
-// up to kBatch experts are all issued before any of them is summed, so a token costs one memory latency per
-// kBatch experts rather than one per expert.  Lane l owns the 16-byte chunks l, l + 64, ... of the row.
+// A token's row is split over wavefronts of 64 chunks of 16 bytes (more, shorter wavefronts measured faster
+// than one per token).  In each, lane e reads the slot map entry of expert e (up to 64 at a time), a ballot
+// gives the experts that took the token, and their rows are summed from the lowest expert up.  The row loads
+// of up to kBatch experts are all issued before any of them is summed, so a token costs one memory latency
+// per kBatch experts rather than one per expert.  Lane l owns the chunks l, l + 64, ... of its wavefront's
+// part of the row.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -16,15 +18,19 @@ namespace crk {
 namespace {
 
 constexpr int kBatch = 4;
+constexpr int kMaxChunks = 1;  // 16-byte chunks per lane: a d = 2048 row is split over 4 wavefronts
 
 template <int CH>  // 16-byte chunks (8 bf16) per lane
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ z, const int32_t* __restrict__ slotmap,
                                                       const float* __restrict__ wt, int T, int E, int C, int d,
-                                                      uint16_t* __restrict__ out) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;  // wave-uniform
+                                                      int split, uint16_t* __restrict__ out) {
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = wv / split;  // `split` wavefronts per token, each over 64 CH consecutive chunks
+    if (t >= T) return;        // wave-uniform
+    const int part = wv - t * split;
     const int lane = threadIdx.x & 63;
     const int nch = d >> 3;
+    const int ch0 = part * 64 * CH;
     float acc[CH][8];
 #pragma unroll
     for (int j = 0; j < CH; ++j)
@@ -51,7 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                     const uint16_t* zr = z + ((int64_t)(e0 + l) * C + cs) * d;
 #pragma unroll
                     for (int j = 0; j < CH; ++j) {
-                        const int ch = lane + 64 * j;
+                        const int ch = ch0 + lane + 64 * j;
                         raw[b][j] = ch < nch ? *reinterpret_cast<const uint4*>(zr + 8 * ch) : make_uint4(0u, 0u, 0u, 0u);
                     }
                     cnt = b + 1;
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int ch = lane + 64 * j;
+        const int ch = ch0 + lane + 64 * j;
         if (ch < nch) {
             uint4 o;
             o.x = pack_bf16x2(acc[j][0], acc[j][1]);
@@ -96,13 +102,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const float* wt, int T, int E, int C, int d,
                           uint16_t* out, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    const int ch = (d / 8 + 63) / 64;
-    const dim3 grid((T + 3) / 4), block(256);
-    if (ch <= 1) combine_kernel<1><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
-    else if (ch <= 2) combine_kernel<2><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
-    else if (ch <= 4) combine_kernel<4><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
-    else if (ch <= 8) combine_kernel<8><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
-    else if (ch <= 16) combine_kernel<16><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, out);
+    // chunks per lane with one wavefront per token, then split over wavefronts to at most kMaxChunks each
+    const int ch_one = (d / 8 + 63) / 64;
+    const int split = (ch_one + kMaxChunks - 1) / kMaxChunks;
+    const int ch = (ch_one + split - 1) / split;
+    const dim3 grid((unsigned)(((int64_t)T * split + 3) / 4)), block(256);
+    if (ch <= 1) combine_kernel<1><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, split, out);
+    else if (ch <= 2) combine_kernel<2><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, split, out);
+    else if (ch <= 4) combine_kernel<4><<<grid, block, 0, st>>>(z, slotmap, wt, T, E, C, d, split, out);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
