@@ -13,6 +13,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kRotqBesideSoftmaxPct = 25;  // share of the token rows rotated in the softmax launch
 constexpr int kMaxRowLen = 8192;           // rotate/quantise keeps a row in registers of one wavefront
 constexpr int64_t kMaxKInt32 = 133144;     // K * 127^2 < 2^31
 
@@ -250,16 +251,20 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
     float* wt = wt_out ? wt_out : b.wt;
     const int64_t S = (int64_t)w->E * C;
 
-    // softmax and the token rotate+quantise share one launch where the shapes allow (they are independent)
-    const hipError_t fused =
-        crk::launch_softmax_rotq(router_logits, T, w->E, b.probs_t, x, w->d, w->group_gu, b.qx, b.sx, stream);
-    if (fused == hipErrorNotSupported) {
+    // The token rotate+quantise does not depend on the routing.  Where the shapes allow, its rows are shared
+    // between the softmax launch and the selection launch, both short and latency-bound, so both fill the chip.
+    const int64_t t1 = (int64_t)T * kRotqBesideSoftmaxPct / 100;
+    const bool split = w->E <= 64 && crk::select_rotq_supported(T, w->E, w->d, w->group_gu);
+    if (split) {
+        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w->E, b.probs_t, x, w->d, w->group_gu, b.qx, b.sx, t1,
+                                         stream));
+        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w->E, C, idx, wt, b.slotmap, x, w->d, w->group_gu, b.qx, b.sx,
+                                        t1, stream));
+    } else {
         CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w->E, b.probs_t, nullptr, stream));
         CRK_TRY(crk::launch_rotq_act(x, T, w->d, w->group_gu, b.qx, b.sx, nullptr, stream));
-    } else {
-        CRK_TRY(fused);
+        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
     }
-    CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
     CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, *w, b.a), stream));
     CRK_TRY(crk::launch_rotq_act(b.a, S, w->I, w->group_dn, b.qa, b.sa, nullptr, stream));
     CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, *w, b.z), stream));

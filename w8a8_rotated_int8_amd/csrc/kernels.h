@@ -25,8 +25,14 @@ hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* 
 // slotmap [E, T] (position of token t in expert e's list, or -1).
 // Router softmax (E <= 64, logits) and token rotate+quantise (fast shapes) in one launch; returns
 // hipErrorNotSupported, having launched nothing, for other shapes.
+// softmax of all T tokens and rotate+quantise of token rows [0, rows) in one launch
 hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, const uint16_t* x, int K,
-                               int group, int8_t* qx, float* sx, hipStream_t st);
+                               int group, int8_t* qx, float* sx, int64_t rows, hipStream_t st);
+// selection of all E experts and rotate+quantise of token rows [row0, T) in one launch
+bool select_rotq_supported(int T, int E, int K, int group);
+hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
+                              const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t row0,
+                              hipStream_t st);
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
                               int32_t* slotmap, hipStream_t st);
 // slotmap [E, T] from idx [E, C].

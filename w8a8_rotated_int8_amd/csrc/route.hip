@@ -125,20 +125,21 @@ __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __res
     softmax_tile(in, is_probs, T, E, probs_t, probs_out, blockIdx.x);
 }
 
-// The router softmax and the token rotate+quantise in one launch: they do not depend on each other, so the
-// first nsm workgroups take softmax tiles and the rest take four token rows each; the rotate+quantise
-// workgroups fill the CUs the short softmax leaves idle, with no second stream to join.
+// The router softmax and token rotate+quantise in one launch: they do not depend on each other, so the first
+// nsm workgroups take softmax tiles and the rest take four token rows each, rows [0, rows); the
+// rotate+quantise workgroups fill the CUs the short softmax leaves idle, with no second stream to join.
 template <int G, int R>
 __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restrict__ logits, int T, int E,
                                                            float* __restrict__ probs_t, int nsm,
                                                            const uint16_t* __restrict__ x, int K,
-                                                           int8_t* __restrict__ qx, float* __restrict__ sx) {
+                                                           int8_t* __restrict__ qx, float* __restrict__ sx,
+                                                           int64_t rows) {
     if ((int)blockIdx.x < nsm) {  // workgroup-uniform
         softmax_tile(logits, 0, T, E, probs_t, nullptr, blockIdx.x);
         return;
     }
     const int64_t row = (int64_t)(blockIdx.x - nsm) * 4 + (threadIdx.x >> 6);
-    if (row >= T) return;  // wave-uniform
+    if (row >= rows) return;  // wave-uniform
     rotq_fast_row<G, R>(x, row, K, qx, sx);
 }
 
@@ -239,15 +240,16 @@ __device__ __forceinline__ int lanes_below(int v, int& total) {
     return below(b0) + 2 * below(b1) + 4 * below(b2);
 }
 
+// Selection of expert e by one workgroup of kSelV wavefronts.
 template <int KR>
-__global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
-                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                   int32_t* __restrict__ slotmap) {
+__device__ __forceinline__ void select_topc_v_block(const float* __restrict__ probs_t, int T, int C,
+                                                    int32_t* __restrict__ idx, float* __restrict__ wt,
+                                                    int32_t* __restrict__ slotmap, int e) {
     __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
     __shared__ uint32_t s_red[2 * kSelV];
     __shared__ uint32_t s_bcast[2];
     __shared__ int s_cnt[2 * kSelV];
-    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float* p = probs_t + (int64_t)e * T;
     const int tb = w * 256 * KR + 4 * lane;  // token of (round j, c): tb + 256 j + c
     const bool vec = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
@@ -434,6 +436,31 @@ __global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* 
     }
 }
 
+template <int KR>
+__global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
+                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
+                                                                   int32_t* __restrict__ slotmap) {
+    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, blockIdx.x);
+}
+
+// The selection and the rest of the token rotate+quantise in one launch: the first E workgroups select (one
+// expert each, a few CUs for a few microseconds), the others take kSelV token rows each from row0 on.
+template <int KR, int G, int R>
+__global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __restrict__ probs_t, int T, int C, int E,
+                                                                 int32_t* __restrict__ idx, float* __restrict__ wt,
+                                                                 int32_t* __restrict__ slotmap,
+                                                                 const uint16_t* __restrict__ x, int K,
+                                                                 int8_t* __restrict__ qx, float* __restrict__ sx,
+                                                                 int64_t row0) {
+    if ((int)blockIdx.x < E) {  // workgroup-uniform
+        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, blockIdx.x);
+        return;
+    }
+    const int64_t row = row0 + (int64_t)(blockIdx.x - E) * kSelV + (threadIdx.x >> 6);
+    if (row >= T) return;  // wave-uniform
+    rotq_fast_row<G, R>(x, row, K, qx, sx);
+}
+
 // Any T: keys re-read from global memory in each pass.
 __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
@@ -542,16 +569,16 @@ hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* 
 }
 
 hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, const uint16_t* x, int K,
-                               int group, int8_t* qx, float* sx, hipStream_t st) {
+                               int group, int8_t* qx, float* sx, int64_t rows, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    if (E > 64 || K % (8 * group) != 0) return hipErrorNotSupported;
+    if (E > 64 || K % (8 * group) != 0 || rows < 0 || rows > T) return hipErrorNotSupported;
     const int nsm = (T + kSmTok - 1) / kSmTok;
-    const int64_t nrot = ((int64_t)T + 3) / 4;
+    const int64_t nrot = (rows + 3) / 4;
     const dim3 grid((unsigned)(nsm + nrot)), block(256);
     const int R = K / (8 * group);
 #define CRK_SR(GG, RR)                                                                                  \
     if (group == GG && R == RR) {                                                                       \
-        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, nsm, x, K, qx, sx);   \
+        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, nsm, x, K, qx, sx, rows); \
         return hipGetLastError();                                                                       \
     }
     CRK_SR(256, 1)
@@ -579,6 +606,35 @@ hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t
 #undef CRK_SEL
     select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap);
     return hipGetLastError();
+}
+
+bool select_rotq_supported(int T, int E, int K, int group) {
+    const int R = (group > 0 && K % (8 * group) == 0) ? K / (8 * group) : 0;
+    return T >= 1 && T <= kSelV * 256 * 8 && E >= 1 && (group == 256 || group == 64) && (R == 1 || R == 2 || R == 4);
+}
+
+hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
+                              const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t row0,
+                              hipStream_t st) {
+    if (!select_rotq_supported(T, E, K, group) || row0 < 0 || row0 > T) return hipErrorNotSupported;
+    const int R = K / (8 * group);
+    const int64_t nrot = (T - row0 + kSelV - 1) / kSelV;
+    const dim3 grid((unsigned)(E + nrot)), block(kSelV * 64);
+#define CRK_SR2(KK, GG, RR)                                                                                 \
+    if (T <= kSelV * 256 * KK && group == GG && R == RR) {                                                  \
+        select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slotmap, x, K, qx, sx, \
+                                                               row0);                                      \
+        return hipGetLastError();                                                                           \
+    }
+#define CRK_SR2_G(KK) CRK_SR2(KK, 256, 1) CRK_SR2(KK, 256, 2) CRK_SR2(KK, 256, 4) CRK_SR2(KK, 64, 1) \
+    CRK_SR2(KK, 64, 2) CRK_SR2(KK, 64, 4)
+    CRK_SR2_G(1)
+    CRK_SR2_G(2)
+    CRK_SR2_G(4)
+    CRK_SR2_G(8)
+#undef CRK_SR2_G
+#undef CRK_SR2
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, hipStream_t st) {
