@@ -87,13 +87,16 @@ def test_rotq_bit_exact(g, K, rows):
 @pytest.mark.parametrize("rows", [1, 7, 37])
 def test_rotq_codes_only_bit_exact(g, K, rows):
     """The codes-only path (no rotated values requested; the layer's own path), including rows whose scale
-    falls below and just above the threshold of the reciprocal-based division."""
+    falls below and just above the threshold of the reciprocal-based division, and a row whose scale is below
+    2^-96 while 2^k times it (the unnormalised transform's scale) is not."""
     say(f"rotq codes g={g} K={K} rows={rows}")
     x = _special_rows(rows, K, 7000 + K + rows)
     if rows >= 7:
         f = synth.bf16_bits_to_f32(x).copy()
         f[5] *= np.float32(2.0 ** -100)         # scale near 2^-107: IEEE division
         f[6] *= np.float32(2.0 ** -80)          # scale near 2^-87: reciprocal-based division
+        if rows >= 8:
+            f[7] *= np.float32(2.0 ** -93)      # scale near 2^-97, unnormalised scale near 2^-94 (g 64) or 2^-93
         x = synth.to_bf16_bits(f)
     q, s, _ = cr.convrot_rotq_rows(dev_bf16(x), g)
     rq, rs = oracle.rotq_rows(x, g)

@@ -14,11 +14,16 @@ namespace {
 // permutations, ^ 4 via a swizzle).  Every stage still forms the pairs (a + b, a - b) of the ascending-h
 // transform, so the fp32 values are those of the plain loop.
 //
-// Quantiser division: with y = 1 / scale rounded to nearest (one IEEE division per row), the quotient
-// q0 = r y, its exact remainder e = fma(-q0, scale, r) and q = fma(e, y, q0) give the correctly rounded
-// r / scale (Markstein's theorem; it needs the remainder to be exact, which holds while scale >= 2^-96 --
-// checked exhaustively on random and half-integer quotients over the whole fp32 range).  Smaller scales
-// take the IEEE division.
+// The transform's sums v are 2^k times the rotated values r = v 2^-k (k = log2(g) / 2, an exact power of
+// two).  With sc = amax|v| / qmax, the row's scale is sc 2^-k and its codes rint(v / sc): while sc >= 2^-96
+// every scaled quantity stays normal, so r / scale and v / sc are the same quotient bit for bit (a v whose
+// r would be subnormal quantises to 0 either way), and the per-element scaling is skipped.  Smaller rows
+// scale each value as defined and take the IEEE division.
+//
+// Quantiser division: with y = 1 / sc rounded to nearest (one IEEE division per row), the quotient q0 = v y,
+// its exact remainder e = fma(-q0, sc, v) and q = fma(e, y, q0) give the correctly rounded v / sc
+// (Markstein's theorem; it needs the remainder to be exact, which holds while sc >= 2^-96 -- checked
+// exhaustively on random and half-integer quotients over the whole fp32 range).
 
 __device__ __forceinline__ float dpp_xor1(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
@@ -86,13 +91,12 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
             mine = __builtin_fmaf(sg1, mine, dpp_xor1(mine));
             mine = __builtin_fmaf(sg2, mine, dpp_xor2(mine));
             mine = __builtin_fmaf(sg4, mine, swz_xor4(mine));
-            mine = mine * kNorm;
-            v[r][e] = mine;
+            v[r][e] = mine;  // 2^k times the rotated value
             amax = fmaxf(amax, fabsf(mine));
         }
     }
     amax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(amax))));  // wave-uniform
-    const float scale = amax / 127.0f;
+    const float sc = amax / 127.0f;
     int8_t* dst = q + row * (int64_t)K + lane * E;
     auto store_round = [&](int r, const uint32_t (&packed)[E / 4]) {
         if constexpr (E == 8) {
@@ -104,8 +108,10 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
                     make_uint4(packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]);
         }
     };
-    if (scale >= 0x1p-96f) {
-        const float y = 1.0f / scale;
+    float scale;
+    if (sc >= 0x1p-96f) {
+        scale = sc * kNorm;  // exact
+        const float y = 1.0f / sc;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t packed[E / 4];
@@ -115,7 +121,7 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float q0 = v[r][e + u] * y;
-                    const float rem = __builtin_fmaf(-q0, scale, v[r][e + u]);
+                    const float rem = __builtin_fmaf(-q0, sc, v[r][e + u]);
                     b[u] = code_bits(__builtin_fmaf(rem, y, q0));
                 }
                 packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
@@ -123,6 +129,7 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
             store_round(r, packed);
         }
     } else {
+        scale = (amax * kNorm) / 127.0f;  // the largest scaled value is the scaled largest value
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t packed[E / 4];
@@ -130,7 +137,7 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
             for (int e = 0; e < E; e += 4) {
                 uint32_t b[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) b[u] = code_bits(scale == 0.0f ? 0.0f : v[r][e + u] / scale);
+                for (int u = 0; u < 4; ++u) b[u] = code_bits(scale == 0.0f ? 0.0f : (v[r][e + u] * kNorm) / scale);
                 packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
             }
             store_round(r, packed);
