@@ -225,6 +225,9 @@ SMALL = [
     synth.MoEShape(T=64, d=256, E=3, I=64, C=64, g_gu=64, g_dn=64),
     synth.MoEShape(T=333, d=512, E=6, I=256, C=1, g_gu=256, g_dn=256),
     synth.MoEShape(T=400, d=512, E=2, I=128, C=300),
+    # d a multiple of 8 g_gu: the token rotate+quantise rides in the routing launches (rows split between them)
+    synth.MoEShape(T=300, d=512, E=8, I=128, C=50, g_gu=64, g_dn=64),
+    synth.MoEShape(T=3, d=512, E=2, I=64, C=2, g_gu=64, g_dn=64),
 ]
 
 
