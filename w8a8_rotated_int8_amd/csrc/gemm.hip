@@ -41,6 +41,8 @@
 //     matrix pipe never waits for a whole stage of fragment reads.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -380,8 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 
     // Epilogue of tile i.  The weights are the MFMA's first operand, so lane l holds activation row l % 32 of
     // each 32 x 32 block and, in register 4 j + i, weight row (output column) 8 j + 4 (l / 32) + i: each lane
-    // owns runs of 4 consecutive output columns, stored as 8 bytes straight from registers, and the gate and
-    // up values of one output sit in the same lane.
+    // owns runs of 4 consecutive output columns, and the gate and up values of one output sit in the same lane.
     auto epilogue = [&](int i) {
         int e, nt, mt;
         decode(i, e, nt, mt);
@@ -426,80 +427,103 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                     b[r] = bf16_to_float(p.bias[n]);
                 }
             };
-            // Two runs j0 < j1 of 4 outputs each, per lane: lanes l and l + 32 hold the two halves of an 8-column
-            // chunk, so one swap between the lane halves hands lane l the whole chunk of run j0 and lane l + 32
-            // the whole chunk of run j1: one 16-byte store each.  Rows that are not 8-aligned fall back to
-            // element stores.  Every store is issued; out-of-range ones are dropped by the buffer range.
+            // One 32 x 32 output block: v[j][x] is this lane's row row0 + l % 32, column colb + 8 j + 4 (l / 32) + x.
+            // Packed to bf16, one swap between the lane halves per pair of runs gives lane l < 32 8-column chunk
+            // j0 of row l and lane l + 32 chunk j1 of the same row (A: chunks 0, 1; B: chunks 2, 3).  One swap
+            // between 16-lane rows then regroups A and B into X (rows 0-15) and Y (rows 16-31), where the four
+            // lanes l % 16 + {0, 16, 32, 48} hold chunks {0, 2, 1, 3} of row l % 16: each 16-byte store writes
+            // 64 contiguous bytes of 16 rows, half the write requests of 32-byte pieces.  Rows that are not
+            // 8-aligned fall back to element stores.  Every store is issued; out-of-range ones are dropped by
+            // the buffer range.
             const bool vec = (ldo & 7) == 0;
-            auto store_pair = [&](int row, int col0, int j0, int j1, const float (&v0)[4], const float (&v1)[4]) {
+            // pk[j][k]: columns 8 j + 4 (l / 32) + 2 k and + 1, packed to bf16
+            auto store_block = [&](int row0, int colb, const uint32_t (&pk)[4][2]) {
                 if (vec) {
-                    const uint32_t a0 = pack_bf16x2(v0[0], v0[1]), a1 = pack_bf16x2(v0[2], v0[3]);
-                    const uint32_t b0 = pack_bf16x2(v1[0], v1[1]), b1 = pack_bf16x2(v1[2], v1[3]);
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                    const int col = col0 - 4 * h + 8 * (h ? j1 : j0);  // first column of this lane's chunk
-                    const int off = col < ldo ? (row * ldo + col) * 2 : kOobOffset;
-                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]}, orsrc,
-                                                           off, 0, 0);
-                    ops += 1;
-                } else {
+                    const auto a0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+                    const auto a1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+                    const auto b0 = __builtin_amdgcn_permlane32_swap(pk[2][0], pk[3][0], false, false);
+                    const auto b1 = __builtin_amdgcn_permlane32_swap(pk[2][1], pk[3][1], false, false);
+                    const uint32_t A[4] = {a0[0], a1[0], a0[1], a1[1]};
+                    const uint32_t B[4] = {b0[0], b1[0], b0[1], b1[1]};
+                    uint32_t X[4], Y[4];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int col = col0 + 8 * (u ? j1 : j0);
+                    for (int k = 0; k < 4; ++k) {
+                        const auto u = __builtin_amdgcn_permlane16_swap(A[k], B[k], false, false);
+                        X[k] = u[0];
+                        Y[k] = u[1];
+                    }
+                    const int col = colb + 8 * (((lane >> 4) & 1) * 2 + ((lane >> 5) & 1));  // chunk {0, 2, 1, 3}
+                    const int r = row0 + (lane & 15);
+                    const int offx = col < ldo ? (r * ldo + col) * 2 : kOobOffset;
+                    const int offy = col < ldo ? ((r + 16) * ldo + col) * 2 : kOobOffset;
+                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)X[0], (int)X[1], (int)X[2], (int)X[3]}, orsrc, offx,
+                                                           0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)Y[0], (int)Y[1], (int)Y[2], (int)Y[3]}, orsrc, offy,
+                                                           0, 0);
+                    ops += 2;
+                } else {
+                    const int r = row0 + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int col = colb + 8 * j + 4 * h;
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            const int off = col + x < ldo ? (row * ldo + col + x) * 2 : kOobOffset;
-                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)float_to_bf16(u ? v1[x] : v0[x]), orsrc, off, 0,
-                                                                  0);
+                            const int off = col + x < ldo ? (r * ldo + col + x) * 2 : kOobOffset;
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk[j][x >> 1] >> (16 * (x & 1))), orsrc, off,
+                                                                  0, 0);
                         }
                     }
-                    ops += 8;
+                    ops += 16;
                 }
             };
             if constexpr (EPI == Epi::kBf16) {
                 // weight block outer, so only one block's scales and bias are live
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    float cs[16];
-                    load_cs(q, cs);
-                    const int col0 = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 4 * h;
-                    auto rows_out = [&](bool with_bias, const float (&bias)[16]) {
+                    const int colb = wblk(q ? my_blk1 : my_blk0, nt) * 32;
+                    auto rows_out = [&](auto with_bias, const float (&bias)[16]) {
 #pragma unroll
                         for (int tm = 0; tm < TM; ++tm) {
                             const float sx = srow[tm * 32 + (lane & 31)];
-                            const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
-                            float v[4][4];
+                            // the block's column scales, read again for each row block: fewer live registers
+                            float cs[16];
+                            load_cs(q, cs);
+                            uint32_t pk[4][2];
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                                for (int x = 0; x < 4; ++x) {
-                                    float t = (float)acc[tm][q][4 * j + x];
-                                    t = t * sx;
-                                    t = t * cs[4 * j + x];
-                                    if (with_bias) t = t + bias[4 * j + x];
-                                    v[j][x] = t;
+                                for (int k = 0; k < 2; ++k) {
+                                    float t[2];
+#pragma unroll
+                                    for (int y = 0; y < 2; ++y) {
+                                        const int r = 4 * j + 2 * k + y;
+                                        t[y] = (float)acc[tm][q][r];
+                                        t[y] = t[y] * sx;
+                                        t[y] = t[y] * cs[r];
+                                        if constexpr (decltype(with_bias)::value) t[y] = t[y] + bias[r];
+                                    }
+                                    pk[j][k] = pack_bf16x2(t[0], t[1]);
                                 }
-                            store_pair(row, col0, 0, 1, v[0], v[1]);
-                            store_pair(row, col0, 2, 3, v[2], v[3]);
+                            store_block(mh * HALF + tm * 32, colb, pk);
                         }
                     };
                     if (p.bias) {  // uniform: one copy of the loop per case
                         float bias[16];
                         load_bias(q, bias);
-                        rows_out(true, bias);
+                        rows_out(std::true_type{}, bias);
                     } else {
-                        rows_out(false, cs);
+                        float unused[16];
+                        rows_out(std::false_type{}, unused);
                     }
                 }
             } else {
                 float cg[16], cu[16];
                 load_cs(0, cg);
                 load_cs(1, cu);
-                const int col0 = wblk(my_blk0, nt) * 32 + 4 * h;  // gate block index = output column block
+                const int colb = wblk(my_blk0, nt) * 32;  // gate block index = output column block
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
                     const float sx = srow[tm * 32 + (lane & 31)];
-                    const int row = mh * HALF + tm * 32 + (lane & 31);  // row within the tile
                     // gate and up rounded to bf16 in one conversion; the gate's bits index the activation table
                     uint32_t gu[16];
                     float sg[16];
@@ -527,13 +551,16 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                         for (int r = 0; r < 16; ++r)
                             if ((gu[r] & 0x7fffu) - kSiluLo >= kSiluSpan) sg[r] = silu_fixed(__uint_as_float(gu[r] << 16));
                     }
-                    float a[4][4];
+                    uint32_t pk[4][2];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) a[j][x] = sg[4 * j + x] * __uint_as_float(gu[4 * j + x] & 0xffff0000u);
-                    store_pair(row, col0, 0, 1, a[0], a[1]);
-                    store_pair(row, col0, 2, 3, a[2], a[3]);
+                        for (int k = 0; k < 2; ++k) {
+                            const int r = 4 * j + 2 * k;
+                            pk[j][k] = pack_bf16x2(sg[r] * __uint_as_float(gu[r] & 0xffff0000u),
+                                                   sg[r + 1] * __uint_as_float(gu[r + 1] & 0xffff0000u));
+                        }
+                    store_block(mh * HALF + tm * 32, colb, pk);
                 }
             }
         }
