@@ -5,6 +5,9 @@ the tokens, grouped INT8 gate/up GEMM with SwiGLU, rotate+quantise of the hidden
 probability-weighted combine.  Weights are converted once before timing (offline in the method).  Inputs are
 resident in HBM when the timed region starts.
 
+--workload dense times one dense W8A8 ConvRot linear over the same 8192 tokens instead (rotate+quantise of the
+tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection).
+
 Prints one JSON line (see --help for options).  --gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -95,6 +98,103 @@ def cpu_baseline(x, lg, w_gu, w_dn, s, n_experts: int, min_seconds: float = 10.0
                       f"work), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s, scaled to TOPS"}
 
 
+def dense_cpu_baseline(x, q, s, g, b, M, K, N, min_seconds: float = 10.0):
+    """Time the CPU oracle's linear (as it stands) on the same [M, K] tokens, repeated until about `min_seconds`
+    of CPU time; weight conversion not timed."""
+    import oracle
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt < min_seconds and reps < 64):
+        t0 = time.perf_counter()
+        oracle.linear_w8a8(x, q, s, g, b)
+        dt += time.perf_counter() - t0
+        reps += 1
+    ops = 2.0 * M * N * K * reps
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"the whole linear (M={M}, K={K}, N={N}), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s"}
+
+
+def run_dense(args):
+    import torch
+    from w8a8_rotated_int8_amd import binding as cr
+    from w8a8_rotated_int8_amd import synth
+
+    dev = torch.device("cuda:0")
+    name = args.dense_shape
+    M, K, N, g = synth.DENSE_SHAPES[name]
+    with_bias = name == "out"
+    print(f"bench: dense {name} M={M} K={K} N={N} g={g} bias={with_bias}", file=sys.stderr, flush=True)
+    x, w, b = synth.dense_linear_inputs(M, K, N, with_bias)
+
+    def bf16_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xd, bd = bf16_dev(x), (None if b is None else bf16_dev(b))
+    qw, sw = cr.convrot_quantize_weights(bf16_dev(w), g, 8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cr.convrot_linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cr.convrot_linear_w8a8(xd, qw, sw, g, bias=bd, y=y, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # dominant kernel: the GEMM stage on the step's token codes, HIP events on its stream
+    qx, sx, _ = cr.convrot_rotq_rows(xd, g)
+    for _ in range(3):
+        cr.convrot_gemm_w8a8_bf16(qx, sx, qw, sw, bias=bd, y=y, stream=stream)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(args.kernel_iters):
+        cr.convrot_gemm_w8a8_bf16(qx, sx, qw, sw, bias=bd, y=y, stream=stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    k_us = k0.elapsed_time(k1) / args.kernel_iters * 1e3
+    ops = 2.0 * M * N * K
+    gemm_tops = ops / (k_us * 1e-6) / 1e12
+    gemm_bytes = M * K + N * K + M * 4 + N * 4 + (N * 2 if with_bias else 0) + M * N * 2
+    print(f"bench: {args.steps} steps, {ms * 1e3:.1f} us/step; GEMM {k_us:.1f} us/launch, {gemm_tops:.0f} TOPS",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "effective INT8 TOPS of one dense W8A8 ConvRot linear (rotate+quantise + GEMM + dequant)",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x20, N(0,0.02) weights"
+                + (" and bias" if with_bias else "") + ")",
+        "config": {"workload": f"dense W8A8 ConvRot linear ({name}) M={M} K={K} N={N} group={g}"
+                               + (" with bias" if with_bias else ""), "M": M, "K": K, "N": N, "group": g},
+        "tokens_per_s": round(M / (ms * 1e-3), 1),
+        "roofline": {"kernel": "dense INT8 GEMM + dequant (convrot_gemm_w8a8_bf16)", "bound": "mfma",
+                     "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": None, "launch_us": round(k_us, 2),
+                     "hbm_frac": round(gemm_bytes / (k_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_experts > 0:
+        import oracle
+        q, s = oracle.quantize_weights(w, g, 8)
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = dense_cpu_baseline(x, q, s, g, b, M, K, N)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,12 +202,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3], help="2: T=2048 C=64; 3: T=8192 C=256")
     ap.add_argument("--wbits", type=int, default=8, choices=[8, 4])
-    ap.add_argument("--cpu-experts", type=int, default=64, help="experts in the CPU-oracle sample (0 = skip)")
-    ap.add_argument("--kernel-iters", type=int, default=50, help="timed launches of the gate/up stage")
+    ap.add_argument("--cpu-experts", type=int, default=64,
+                    help="experts in the CPU-oracle sample of the MoE workload; 0 skips the CPU baseline (either workload)")
+    ap.add_argument("--kernel-iters", type=int, default=50, help="timed launches of the dominant kernel")
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense"])
+    ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
                  "(expert-parallel sharding is described in the design notes, not built)")
+    if args.workload == "dense":
+        return run_dense(args)
 
     import torch
     from w8a8_rotated_int8_amd import binding as cr

@@ -175,6 +175,16 @@ convrot_status convrot_quantize_prerotated(const float* r, int64_t rows, int K, 
 convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int N, int K, int32_t* acc_out,
                                    hipStream_t stream);
 
+/* The linear's GEMM stage on quantised tokens: y[M, N] = bf16( ((float)(qx . qw^T) * sx) * sw ) (+ bias),
+ * the second half of convrot_linear_w8a8 ("Nucleus-Image INT8 Convrot Experts", "Quantization": W8A8
+ * ConvRot linear with BF16 output; dequantisation as in that entry point).  qx (device) [M, K] int8 codes and
+ * sx (device) [M] fp32 scales of the rotated rows (convrot_rotq_rows with the weights' group); qw (device)
+ * [N, K] int8 codes in CONVROT_LAYOUT_MFMA; sw (device) [N]; bias (device) [N] bf16 or NULL; y (device)
+ * [M, N] bf16.  Requires M, N >= 1, 64 <= K <= 8192, K % 64 == 0. */
+convrot_status convrot_gemm_w8a8_bf16(const int8_t* qx, const float* sx, int M, int K, const int8_t* qw,
+                                      const float* sw, int N, const uint16_t* bias, uint16_t* y,
+                                      hipStream_t stream);
+
 /* Bytes of workspace moe_route_expert_choice needs. */
 size_t moe_route_workspace_bytes(int T, int E);
 

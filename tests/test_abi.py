@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
@@ -91,6 +91,9 @@ def test_stage_validation(L):
     assert L.convrot_gemm_i8_i32(P, P, 4, 4, 24, P, None) == SHAPE
     assert L.convrot_gemm_i8_i32(P, P, 4, 4, 140000, P, None) == SHAPE
     assert L.convrot_gemm_i8_i32(P, None, 4, 4, 32, P, None) == NULL
+    assert L.convrot_gemm_w8a8_bf16(P, P, 4, 96, P, P, 8, None, P, None) == SHAPE  # K % 64
+    assert L.convrot_gemm_w8a8_bf16(P, P, 0, 128, P, P, 8, None, P, None) == SHAPE
+    assert L.convrot_gemm_w8a8_bf16(P, None, 4, 128, P, P, 8, None, P, None) == NULL
     nb = L.moe_route_workspace_bytes(100, 8)
     assert nb >= 100 * 8 * 4
     assert L.moe_route_expert_choice(P, 0, 100, 8, 101, P, P, None, P, nb, None) == SHAPE

@@ -8,7 +8,10 @@ BF16 within 1e-2 relative (and, the arithmetic being fully specified, expected b
 
   * T = 2048, C = 64 and T = 8192, C = 256 layers (64 experts, d = 2048, I = 1536), host-generated inputs;
   * the 29-layer stack: layers 0 and 28 with 8-bit weights and layer 0 with 4-bit weights (weights drawn on the
-    GPU by torch's generator, copied to the host for the oracle).
+    GPU by torch's generator, copied to the host for the oracle);
+  * dense W8A8 ConvRot linears over the same T = 8192 tokens (fused qkv, an FFN-down-like [2048, 8192] and the
+    attention output projection with group 64 and a bias), through the linear entry point and through its GEMM
+    stage from the oracle's token codes.
 """
 import numpy as np
 import pytest
@@ -94,3 +97,24 @@ def test_layer_stack(layer, bits):
     w_gu = host_bf16(w_gu_d)
     w_dn = host_bf16(w_dn_d)
     _check_layer(x, lg, w_gu_d, w_dn_d, w_gu, w_dn, s, bits, what)
+
+
+@pytest.mark.parametrize("name", list(synth.DENSE_SHAPES))
+def test_dense_linear_full_size(name):
+    M, K, N, g = synth.DENSE_SHAPES[name]
+    with_bias = name == "out"
+    say(f"dense {name}: M={M} K={K} N={N} g={g} bias={with_bias}")
+    x, w, b = synth.dense_linear_inputs(M, K, N, with_bias)
+    qw, sw = cr.convrot_quantize_weights(dev_bf16(w), g, 8)
+    rqw, rsw = oracle.quantize_weights(w, g, 8)
+    assert np.array_equal(untile_codes(host(qw), 1, N, K, 8)[0], rqw), "weight codes"
+    assert np.array_equal(host(sw).view(np.uint32), rsw.view(np.uint32)), "weight scales"
+    bd = None if b is None else dev_bf16(b)
+    y = cr.convrot_linear_w8a8(dev_bf16(x), qw, sw, g, bias=bd)
+    say(f"dense {name}: oracle")
+    ry, rqx, rsx = oracle.linear_w8a8(x, rqw, rsw, g, b)
+    exact = assert_bf16_within(host_bf16(y), ry, what=f"dense {name}")
+    say(f"dense {name}: {exact * 100:.3f}% bit-identical")
+    assert exact == 1.0
+    y2 = cr.convrot_gemm_w8a8_bf16(dev(rqx), dev(rsx), qw, sw, bias=bd)
+    assert np.array_equal(host_bf16(y2), ry), "GEMM stage"

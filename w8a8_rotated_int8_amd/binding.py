@@ -49,6 +49,7 @@ _SIGS = {
     "convrot_rotq_rows": (_i, [_p, _i64, _i, _i, _p, _p, _p, _p]),
     "convrot_quantize_prerotated": (_i, [_p, _i64, _i, _i, _p, _p, _p]),
     "convrot_gemm_i8_i32": (_i, [_p, _p, _i, _i, _i, _p, _p]),
+    "convrot_gemm_w8a8_bf16": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (_sz, [_i, _i]),
     "moe_route_expert_choice": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
     "moe_gateup_swiglu": (_i, [_p, _p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p]),
@@ -250,6 +251,17 @@ def convrot_quantize_prerotated(r, bits: int = 8, q_out=None, s_out=None, stream
     _check("convrot_quantize_prerotated", lib().convrot_quantize_prerotated(
         _ptr(r), rows, K, bits, _ptr(q_out), _ptr(s_out), _stream(stream)))
     return q_out, s_out
+
+
+def convrot_gemm_w8a8_bf16(qx, sx, qw, sw, bias=None, y=None, stream=None):
+    """The linear's GEMM + dequant on quantised tokens qx [M, K] int8, sx [M]; qw in the MFMA layout."""
+    M, K = qx.shape
+    N = sw.shape[0]
+    if y is None:
+        y = _empty((M, N), torch.bfloat16, qx)
+    _check("convrot_gemm_w8a8_bf16", lib().convrot_gemm_w8a8_bf16(
+        _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y), _stream(stream)))
+    return y
 
 
 def convrot_gemm_i8_i32(a, b, acc_out=None, stream=None):

@@ -206,6 +206,17 @@ convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t
     int8_t* qx = cv.take<int8_t>((size_t)M * K);
     float* sx = cv.take<float>((size_t)M);
     CRK_TRY(crk::launch_rotq_act(x, M, K, group, qx, sx, nullptr, stream));
+    return convrot_gemm_w8a8_bf16(qx, sx, M, K, qw, sw, N, bias, y, stream);
+}
+
+convrot_status convrot_gemm_w8a8_bf16(const int8_t* qx, const float* sx, int M, int K, const int8_t* qw,
+                                      const float* sw, int N, const uint16_t* bias, uint16_t* y,
+                                      hipStream_t stream) {
+    if (!qx || !sx || !qw || !sw || !y) return CONVROT_ERR_NULL;
+    if (M < 1 || N < 1 || K < 64 || K > kMaxRowLen || K % 64) return CONVROT_ERR_SHAPE;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) || !aligned16(y) ||
+        (bias && !aligned16(bias)))
+        return CONVROT_ERR_ALIGN;
     crk::GemmProblem p{};
     p.A = qx;
     p.a_rows = nullptr;
@@ -222,8 +233,7 @@ convrot_status convrot_linear_w8a8(const uint16_t* x, int M, int K, const int8_t
     p.bias = bias;
     p.out = y;
     p.epi = crk::Epi::kBf16;
-    CRK_TRY(crk::launch_grouped_gemm(p, stream));
-    return CONVROT_OK;
+    return hip_status(crk::launch_grouped_gemm(p, stream));
 }
 
 size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights* w) {

@@ -10,11 +10,12 @@ Recipe
   * numpy ``Generator(PCG64(seed))`` draws ``standard_normal`` in fp32, scaled in fp32, then rounded to bf16
     (nearest-even, via torch); bf16 tensors are returned as raw ``uint16`` bits on the host.
   * seed = 1000 * config + role; roles: x = 1, W (or W_gu) = 2, W_dn = 3, router logits = 4, outlier channel
-    choice = 5.
+    choice = 5, bias = 6.  The dense linears at large M (attention and FFN projections of the same T = 8192
+    tokens) use seed base 5000.
   * Activations ~ N(0, 1) with floor(1% of d) outlier feature columns (the same for every token, chosen by the
     role-5 generator without replacement) multiplied by 20 before the bf16 rounding; the single-linear case
     uses 4 outlier columns of 512.
-  * Weights ~ N(0, 0.02); router logits fp32 ~ N(0, 1).
+  * Weights ~ N(0, 0.02); router logits fp32 ~ N(0, 1); biases ~ N(0, 0.02).
   * The 29-layer stack draws on the GPU with torch's generator, seed = 4000 + 10 * layer + role, because 17.5 G
     host draws would dominate the run; each layer reuses the same x.
 """
@@ -24,7 +25,11 @@ from dataclasses import dataclass
 
 import numpy as np
 
-ROLE_X, ROLE_W, ROLE_WDN, ROLE_LOGITS, ROLE_OUTLIER = 1, 2, 3, 4, 5
+ROLE_X, ROLE_W, ROLE_WDN, ROLE_LOGITS, ROLE_OUTLIER, ROLE_BIAS = 1, 2, 3, 4, 5, 6
+DENSE_SEED_BASE = 5000
+# Dense W8A8 ConvRot linears over the T = 8192 tokens of d = 2048: fused qkv [6144, 2048], FFN-down-like
+# [2048, 8192] and the attention output projection [2048, 2048] (M, K, N, group).
+DENSE_SHAPES = {"qkv": (8192, 2048, 6144, 256), "ffn_down": (8192, 8192, 2048, 256), "out": (8192, 2048, 2048, 64)}
 OUTLIER_GAIN = 20.0
 W_STD = 0.02
 
@@ -100,6 +105,15 @@ def linear_inputs(cfg: int = 0, M=None, K=None, N=None, n_outlier=None):
     n_outlier = c["n_outlier"] if n_outlier is None else n_outlier
     base = 1000 * cfg
     return activations(base, M, K, n_outlier), weights(base + ROLE_W, (N, K))
+
+
+def dense_linear_inputs(M: int, K: int, N: int, with_bias: bool = False):
+    """x [M, K], W [N, K] and optionally a bias [N] (bf16 bits) for a dense linear at large M."""
+    base = DENSE_SEED_BASE
+    x = activations(base, M, K, max(1, K // 100))
+    w = weights(base + ROLE_W, (N, K))
+    b = weights(base + ROLE_BIAS, (N,)) if with_bias else None
+    return x, w, b
 
 
 def moe_inputs(cfg: int, shape: MoEShape | None = None, seed_base: int | None = None):
