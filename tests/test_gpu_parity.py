@@ -83,7 +83,8 @@ def test_rotq_bit_exact(g, K, rows):
     assert np.array_equal(host(q), rq)
 
 
-@pytest.mark.parametrize("g,K", [(64, 512), (64, 1536), (64, 4096), (256, 2048), (256, 4096), (256, 8192)])
+@pytest.mark.parametrize("g,K", [(64, 512), (64, 1536), (64, 3072), (64, 4096), (256, 2048), (256, 4096),
+                                 (256, 8192)])
 @pytest.mark.parametrize("rows", [1, 7, 37])
 def test_rotq_codes_only_bit_exact(g, K, rows):
     """The codes-only path (no rotated values requested; the layer's own path), including rows whose scale

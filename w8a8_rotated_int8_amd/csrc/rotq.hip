@@ -213,6 +213,18 @@ __global__ __launch_bounds__(256) void rotq_act_fast_kernel(const uint16_t* __re
     rotq_fast_row<G, R>(x, row, K, q, s);
 }
 
+// Long rows (R = K / 8g above 1 for g = 256, above 4 for g = 64): WPR wavefronts share a row, RW rounds each, and
+// take its maximum from one another through LDS.  One round of g = 256 per lane holds 54 VGPRs where four hold
+// 217, so the split runs 8 wavefronts per SIMD instead of 2.
+template <int G, int RW, int WPR>
+__global__ __launch_bounds__(256) void rotq_act_split_kernel(const uint16_t* __restrict__ x, int64_t rows, int K,
+                                                             int8_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ float xch[4];
+    const int w = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + w / WPR;
+    rotq_fast_part<G, RW, WPR>(x, row, row < rows, K, w % WPR, q, s, xch);
+}
+
 // rows: source rows (E * N for weights); N: rows per expert (tiled modes only).
 template <int G, int QMAX, Out OUT, bool CHECK>
 hipError_t launch_nv(const void* x, int64_t rows, int K, int N, void* q, float* s, float* rot, hipStream_t st) {
@@ -250,15 +262,22 @@ hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, in
         rotq_act_fast_kernel<G, RR><<<grid, block, 0, st>>>(x, rows, K, q, s);                   \
         return hipGetLastError();                                                                \
     }
+#define CRK_SPLIT(G, RR, RW, WPR)                                                                          \
+    if (group == G && R == RR) {                                                                           \
+        const dim3 sgrid((unsigned)((rows + 4 / WPR - 1) / (4 / WPR)));                                    \
+        rotq_act_split_kernel<G, RW, WPR><<<sgrid, block, 0, st>>>(x, rows, K, q, s);                      \
+        return hipGetLastError();                                                                          \
+    }
         CRK_FAST(256, 1)
-        CRK_FAST(256, 2)
-        CRK_FAST(256, 4)
+        CRK_SPLIT(256, 2, 1, 2)
+        CRK_SPLIT(256, 4, 1, 4)
         CRK_FAST(64, 1)
         CRK_FAST(64, 2)
         CRK_FAST(64, 3)
         CRK_FAST(64, 4)
-        CRK_FAST(64, 6)
-        CRK_FAST(64, 8)
+        CRK_SPLIT(64, 6, 3, 2)
+        CRK_SPLIT(64, 8, 2, 4)
+#undef CRK_SPLIT
 #undef CRK_FAST
     }
     if (group == 256) return launch_nv<256, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);

@@ -49,19 +49,23 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
     return ab | cd;
 }
 
-// One row per wavefront (row < rows is the caller's check).
-template <int G, int R>
-__device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, int64_t row, int K,
-                                              int8_t* __restrict__ q, float* __restrict__ s) {
+// Rounds [part R, part R + R) of one row by this wavefront; WPR wavefronts of the workgroup (consecutive, this
+// one among them) share the row and exchange their maxima through xch (WPR floats from the group's first
+// wavefront on) behind a workgroup barrier, which every wavefront reaches (valid = false: a row past the end,
+// nothing read or written).  WPR = 1: one row per wavefront, no exchange.
+template <int G, int R, int WPR>
+__device__ __forceinline__ void rotq_fast_part(const uint16_t* __restrict__ x, int64_t row, bool valid, int K, int part,
+                                               int8_t* __restrict__ q, float* __restrict__ s, float* xch) {
     constexpr int E = G / 8;  // elements per lane per round
     const int lane = threadIdx.x & 63;
-    const uint16_t* src = x + row * (int64_t)K + lane * E;
+    const int64_t off0 = row * (int64_t)K + (int64_t)part * R * 8 * G + lane * E;
+    const uint16_t* src = x + off0;
     float v[R][E];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < E / 8; ++c) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c);
+            const uint4 raw = valid ? *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
             const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -96,8 +100,16 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
         }
     }
     amax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(amax))));  // wave-uniform
+    if constexpr (WPR > 1) {
+        const int w = threadIdx.x >> 6, w0 = w - part;
+        if (lane == 0) xch[w] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) amax = fmaxf(amax, xch[w0 + i]);
+    }
+    if (!valid) return;  // wave-uniform, after the barrier
     const float sc = amax / 127.0f;
-    int8_t* dst = q + row * (int64_t)K + lane * E;
+    int8_t* dst = q + off0;
     auto store_round = [&](int r, const uint32_t (&packed)[E / 4]) {
         if constexpr (E == 8) {
             *reinterpret_cast<uint2*>(dst + r * 8 * G) = make_uint2(packed[0], packed[1]);
@@ -143,7 +155,14 @@ __device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, in
             store_round(r, packed);
         }
     }
-    if (lane == 0) s[row] = scale;
+    if (lane == 0 && part == 0) s[row] = scale;
+}
+
+// One row per wavefront (row < rows is the caller's check).
+template <int G, int R>
+__device__ __forceinline__ void rotq_fast_row(const uint16_t* __restrict__ x, int64_t row, int K,
+                                              int8_t* __restrict__ q, float* __restrict__ s) {
+    rotq_fast_part<G, R, 1>(x, row, true, K, 0, q, s, nullptr);
 }
 
 }  // namespace
