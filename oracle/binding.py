@@ -15,7 +15,7 @@ __all__ = [
     "build", "load", "bf16_round", "bf16_to_f32", "exp", "silu", "rotate_rows_f32", "rotate_rows_bf16",
     "quantize_rows", "rotq_rows", "pack_int4", "unpack_int4", "quantize_weights", "gemm_i8_i32",
     "dequant_bf16", "linear_w8a8", "softmax_experts", "route_from_probs", "route", "swiglu", "combine",
-    "moe_gateup", "moe_down", "moe_forward", "moe_rows",
+    "moe_gateup", "moe_down", "moe_forward", "moe_rows", "philox4x64_10", "requantize_lora",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +65,9 @@ def _declare(lib):
         "oracle_pack_int4": (None, [_p, _i64, _i, _p]),
         "oracle_unpack_int4": (None, [_p, _i64, _i, _p]),
         "oracle_quantize_weights": (_i, [_p, _i, _i, _i, _i, _i, _p, _p]),
+        "oracle_philox4x64_10": (None, [_p, _p, _p]),
+        "oracle_requantize_lora": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _i, ctypes.c_float, ctypes.c_uint64, _p,
+                                        _p]),
         "oracle_gemm_i8_i32": (None, [_p, _p, _i, _i, _i, _p]),
         "oracle_dequant_bf16": (None, [_p, _p, _p, _p, _i, _i, _p]),
         "oracle_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p]),
@@ -183,6 +186,32 @@ def unpack_int4(p, K: int) -> np.ndarray:
     out = np.empty(p.shape[:-1] + (K,), np.int8)
     load().oracle_unpack_int4(_ptr(p), p.size // (K // 2), K, _ptr(out))
     return out
+
+
+def philox4x64_10(ctr, key) -> np.ndarray:
+    """The four 64-bit words of Philox4x64-10 at counter ctr (4 words) and key (2 words)."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.empty(4, np.uint64)
+    load().oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def requantize_lora(q, s, g: int, lb, la, alpha: float, seed: int):
+    """q int8 [E, N, K] (or [N, K]), s [E, N]; lb bf16 bits [E, N, r], la [E, r, K] (or without E).
+    Returns (codes int8, scales fp32) of the LoRA-patched weights, re-quantised with random rounding."""
+    q = _c(q, np.int8)
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, s, lb, la = q[None], np.asarray(s)[None], np.asarray(lb)[None], np.asarray(la)[None]
+    s, lb, la = _c(s, np.float32), _c(lb, np.uint16), _c(la, np.uint16)
+    E, N, K = q.shape
+    r = lb.shape[-1]
+    qo = np.empty_like(q)
+    so = np.empty((E, N), np.float32)
+    _check(load().oracle_requantize_lora(_ptr(q), _ptr(s), E, N, K, g, _ptr(lb), _ptr(la), r, float(alpha),
+                                         int(seed), _ptr(qo), _ptr(so)), "requantize_lora")
+    return (qo[0], so[0]) if squeeze else (qo, so)
 
 
 def quantize_weights(w, g: int, bits: int = 8):

@@ -23,7 +23,10 @@
  *         tokens, outputs are scattered back through one matmul); MoE expert SwiGLU is silu(gate)*up
  *         with the first half of the fused projection the gate and the second half the up projection.
  *  [XB]   "XB_UNetLoaderINTROCm" node page, "The mechanism, briefly": matmuls multiply in INT8 and
- *         dequantise back on the fly.
+ *         dequantise back on the fly; "Inputs that matter": a stochastic LoRA mode bakes LoRAs into the
+ *         quantised model with random-rounding deltas at load.
+ *  [NF2s] The NitroFusion2 page, "Why a step-1 file": a LoRA patched onto a quantised file is
+ *         re-quantised with fresh scales and random rounding.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - Hadamard: Sylvester construction, natural order, no random signs; block-diagonal with contiguous
@@ -43,6 +46,12 @@
  *  - Combine: out[t] = bf16( sum over experts e ascending that took t of w * z ), accumulated in fp32
  *    starting from +0.0f with a separate multiply and add; tokens taken by no expert give +0.
  *  - INT4 packing: two's-complement nibbles, even k in bits 0-3, odd k in bits 4-7.
+ *  - LoRA re-quantisation (oracle_requantize_lora): the patch is applied in the rotated basis to the
+ *    dequantised weights, the delta alpha * B A rotated like the weights; fresh scale amax / 127; random
+ *    rounding floor(t) + [u < t - floor(t)] with u uniform in [0, 1) from Philox4x64-10 (a counter-based
+ *    generator, see oracle_philox4x64_10): counter ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0), word
+ *    k % 4, top 24 bits times 2^-24.  Delta sums in ascending rank index from +0.0f, separate multiply and
+ *    add, then times alpha.  The pages fix none of these details; parity pinned by the tests below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -257,6 +266,109 @@ int oracle_quantize_weights(const uint16_t* w, int E, int N, int K, int g, int b
     }
     free(q);
     return st;
+}
+
+/* ------------------------------------------------------------------------------------------------- */
+/* Counter-based random numbers: Philox4x64 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel    */
+/* random numbers: as easy as 1, 2, 3", SC 2011).  Each round multiplies counter words 0 and 2 by the    */
+/* two Philox constants (full 128-bit products), and the new counter is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),  */
+/* hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key is bumped by the two Weyl constants before every round but   */
+/* the first.                                                                                          */
+/* ------------------------------------------------------------------------------------------------- */
+
+static void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
+    unsigned __int128 p = (unsigned __int128)a * (unsigned __int128)b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+void oracle_philox4x64_10(const uint64_t* ctr, const uint64_t* key, uint64_t* out) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        uint64_t hi0, lo0, hi1, lo1;
+        mulhilo64(M0, c0, &hi0, &lo0);
+        mulhilo64(M1, c2, &hi1, &lo1);
+        uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* ------------------------------------------------------------------------------------------------- */
+/* LoRA patch of quantised weights with re-quantisation  [NF2s], [XB]                                  */
+/* ------------------------------------------------------------------------------------------------- */
+
+/* q [E, N, K] int8 and s [E, N]: weights quantised in the rotated basis (group g).  lb [E, N, rank] and
+ * la [E, rank, K] bf16: the LoRA factors (original basis), delta = alpha * lb . la.  Writes fresh codes
+ * q_out [E, N, K] and scales s_out [E, N]:
+ *   R = (float)q * s;  D[k] = alpha * sum_j lb[n, j] * la[j, k];  V = R + rotate_g(D);
+ *   scale = amax|V| / 127;  t = V / scale (0 when scale is 0);
+ *   code = clamp(floor(t) + (u < t - floor(t) ? 1 : 0), -127, 127): rounded up with probability t - floor(t)
+ *   (the difference is exact in fp32), so integers stay put and the rounding is unbiased to 2^-24. 
+ * Returns 0, or -1 on a bad group or K (K must be a multiple of g and of 4). */
+int oracle_requantize_lora(const int8_t* q, const float* s, int E, int N, int K, int g, const uint16_t* lb,
+                           const uint16_t* la, int rank, float alpha, uint64_t seed, int8_t* q_out,
+                           float* s_out) {
+    int k4 = log4_of(g);
+    if (k4 < 0 || K % g || K % 4 || rank < 0) return -1;
+    float norm = ldexpf(1.0f, -k4);
+    int64_t rows = (int64_t)E * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t e = row / N;
+        float* d = (float*)malloc(sizeof(float) * (size_t)K);
+        float* v = (float*)malloc(sizeof(float) * (size_t)K);
+        for (int k = 0; k < K; ++k) {
+            float acc = 0.0f;
+            for (int j = 0; j < rank; ++j) {
+                float p = bf16_to_f32(lb[row * rank + j]) * bf16_to_f32(la[(e * rank + j) * (int64_t)K + k]);
+                acc = acc + p;
+            }
+            d[k] = alpha * acc;
+        }
+        for (int b = 0; b < K; b += g) fwht_block(d + b, g, norm);
+        float amax = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float r = (float)q[row * (int64_t)K + k] * s[row];
+            v[k] = r + d[k];
+            float a = fabsf(v[k]);
+            if (a > amax) amax = a;
+        }
+        float sc = amax / 127.0f;
+        s_out[row] = sc;
+        uint64_t key[2] = {seed, 0}, ctr[4] = {0, 0, 0, 0}, w[4];
+        for (int k = 0; k < K; ++k) {
+            if (k % 4 == 0) {
+                ctr[0] = (uint64_t)row * (uint64_t)(K / 4) + (uint64_t)(k / 4);
+                oracle_philox4x64_10(ctr, key, w);
+            }
+            float u = (float)(w[k % 4] >> 40) * 0x1p-24f;
+            float c = 0.0f;
+            if (sc != 0.0f) {
+                float t = v[k] / sc;
+                float fl = floorf(t);
+                c = fl + (u < t - fl ? 1.0f : 0.0f);
+                if (c > 127.0f) c = 127.0f;
+                if (c < -127.0f) c = -127.0f;
+            }
+            q_out[row * (int64_t)K + k] = (int8_t)c;
+        }
+        free(d);
+        free(v);
+    }
+    return 0;
 }
 
 /* ------------------------------------------------------------------------------------------------- */

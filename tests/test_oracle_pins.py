@@ -389,3 +389,97 @@ def test_moe_rows_equals_full_layer_at_every_token(orc):
     r = orc.moe_forward(x, lg, s.C, q_gu, s_gu, 256, q_dn, s_dn, 64, intermediates=True)
     rows = orc.moe_rows(r["qx"], r["sx"], r["idx"], r["wt"], q_gu, s_gu, q_dn, s_dn, 64, np.arange(s.T))
     assert np.array_equal(rows, r["out"])
+
+
+# ----------------------------------------------------------------------------------------------------------
+# LoRA re-quantisation with random rounding (NitroFusion2 page, "Why a step-1 file"; XB loader, lora_mode)
+# ----------------------------------------------------------------------------------------------------------
+
+def _np_philox(ctr, key):
+    """numpy's own Philox4x64-10 bit generator, which advances its counter by one before each block."""
+    c = [int(v) for v in ctr]
+    c[0] = (c[0] - 1) % (1 << 64)  # every test counter has word 0 >= 1: no borrow
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(c, dtype=np.uint64))
+    return bg.random_raw(4)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_philox_matches_numpy_bit_generator(orc, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        ctr = [int(rng.integers(1, 1 << 63)), int(rng.integers(0, 1 << 63)), int(rng.integers(0, 1 << 63)),
+               int(rng.integers(0, 1 << 63))]
+        key = [int(rng.integers(0, 1 << 63)), int(rng.integers(0, 1 << 63))]
+        assert np.array_equal(orc.philox4x64_10(ctr, key), _np_philox(ctr, key))
+
+
+def _quantised_rows(rng, E, N, K, pow2_scales=False):
+    q = rng.integers(-127, 128, (E, N, K)).astype(np.int8)
+    q[..., 1] = 127  # every row reaches qmax
+    if pow2_scales:
+        s = np.ldexp(np.float32(1.0), rng.integers(-12, -4, (E, N))).astype(np.float32)
+    else:
+        s = (rng.random((E, N)) * 1e-3 + 1e-4).astype(np.float32)
+    return q, s
+
+
+def test_lora_requant_without_delta_keeps_codes(orc):
+    """No delta and power-of-two scales: every value is exactly code * scale, the fresh scale is the old one and
+    every quotient an integer, so the random rounding returns the codes unchanged."""
+    rng = np.random.default_rng(3)
+    q, s = _quantised_rows(rng, 2, 8, 512, pow2_scales=True)
+    lb = synth.to_bf16_bits(rng.standard_normal((2, 8, 4)).astype(np.float32))
+    la = synth.to_bf16_bits(rng.standard_normal((2, 4, 512)).astype(np.float32))
+    for rank_b, rank_a, alpha in [(lb[..., :0], la[:, :0], 1.0), (lb, la, 0.0)]:
+        q2, s2 = orc.requantize_lora(q, s, 64, rank_b, rank_a, alpha, seed=7)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+def test_lora_requant_follows_the_rotated_patch(orc):
+    """Codes are floor or ceil of V / scale with V = R + rotate(alpha B A) computed in fp64 here, and the
+    scale is max|V| / 127 (a dropped term, a wrong sign or a transposed factor moves V far beyond this)."""
+    rng = np.random.default_rng(4)
+    E, N, K, r, g = 2, 6, 512, 8, 64
+    q, s = _quantised_rows(rng, E, N, K)
+    lb = synth.to_bf16_bits((rng.standard_normal((E, N, r)) * 0.05).astype(np.float32))
+    la = synth.to_bf16_bits((rng.standard_normal((E, r, K)) * 0.05).astype(np.float32))
+    alpha = 0.5
+    q2, s2 = orc.requantize_lora(q, s, g, lb, la, alpha, seed=11)
+    bf = synth.bf16_bits_to_f32
+    delta = alpha * np.einsum("enr,erk->enk", bf(lb).astype(np.float64), bf(la).astype(np.float64))
+    h = scipy.linalg.hadamard(g).astype(np.float64) / math.sqrt(g)
+    drot = (delta.reshape(E, N, K // g, g) @ h.T).reshape(E, N, K)
+    v = q.astype(np.float64) * s[..., None].astype(np.float64) + drot
+    sc = np.abs(v).max(axis=-1) / 127
+    np.testing.assert_allclose(s2, sc, rtol=1e-5)
+    t = v / s2[..., None].astype(np.float64)
+    c = q2.astype(np.float64)
+    assert np.all(c >= np.floor(t) - 1e-3 - 1) and np.all(c <= np.ceil(t) + 1e-3)
+    assert np.all((c == np.floor(t + 1e-4)) | (c == np.ceil(t - 1e-4)) | (np.abs(t) > 126.9))
+    assert np.abs(q2.astype(int) - q.astype(int)).max() > 0  # the patch changed something
+
+
+def test_lora_requant_rounding_is_unbiased_and_seeded(orc):
+    """A rank-1 delta constant over a rotation block rotates into one element per block: c * sqrt(g).  With
+    scale 1 that element's quotient is code + 0.3, so it rounds up in about 30 % of the rows; the rest
+    stay exact.  The same seed gives the same codes, another seed other codes."""
+    rng = np.random.default_rng(5)
+    E, N, K, g = 1, 4096, 256, 256
+    q = rng.integers(-100, 100, (E, N, K)).astype(np.int8)
+    q[..., 1] = 127
+    s = np.ones((E, N), np.float32)
+    c = np.float32(0.3 / 16)  # rotate(c * ones) = 16 c at k = 0 (g = 256), bf16-exact? no: use its bf16 value
+    cb = synth.to_bf16_bits(np.array([c], np.float32))
+    cf = float(synth.bf16_bits_to_f32(cb)[0])
+    lb = synth.to_bf16_bits(np.ones((E, N, 1), np.float32))
+    la = np.tile(cb, (E, 1, K)).reshape(E, 1, K)
+    q2, s2 = orc.requantize_lora(q, s, g, lb, la, 1.0, seed=21)
+    assert np.array_equal(s2, s)
+    frac = 16 * cf
+    up = q2[..., 0].astype(int) - q[..., 0].astype(int)
+    assert set(np.unique(up)) <= {0, 1}
+    assert abs(up.mean() - frac) < 0.03, (up.mean(), frac)
+    assert np.array_equal(q2[..., 1:], q[..., 1:])
+    q3, _ = orc.requantize_lora(q, s, g, lb, la, 1.0, seed=21)
+    q4, _ = orc.requantize_lora(q, s, g, lb, la, 1.0, seed=22)
+    assert np.array_equal(q3, q2) and not np.array_equal(q4, q2)
