@@ -6,7 +6,9 @@ probability-weighted combine.  Weights are converted once before timing (offline
 resident in HBM when the timed region starts.
 
 --workload dense times one dense W8A8 ConvRot linear over the same 8192 tokens instead (rotate+quantise of the
-tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection).
+tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection).  --workload lora times the load-time
+LoRA patch of the layer's quantised gate/up weights (64 x [3072, 2048], rank 32), re-quantised with random
+rounding into the layout the GEMM streams.
 
 Prints one JSON line (see --help for options).  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -195,6 +197,86 @@ def run_dense(args):
     print(json.dumps(line), flush=True)
 
 
+PEAK_VALU_OPS = 256 * 64 * 2.4e9 / 1e12  # fp32 VALU operations (no FMA) per second, T: 256 CUs x 64 lanes x 2.4 GHz
+
+
+def run_lora(args):
+    import torch
+    from w8a8_rotated_int8_amd import binding as cr
+    from w8a8_rotated_int8_amd import synth
+
+    dev = torch.device("cuda:0")
+    s3 = synth.CONFIGS[3]
+    E, N, K, g, rank, alpha = s3.E, 2 * s3.I, s3.d, s3.g_gu, 32, 0.5
+    print(f"bench: lora E={E} N={N} K={K} g={g} rank={rank}", file=sys.stderr, flush=True)
+    gen = torch.Generator(device=dev).manual_seed(3000)
+    w = (torch.randn((E, N, K), generator=gen, device=dev) * synth.W_STD).to(torch.bfloat16)
+    q, s = cr.convrot_quantize_weights(w, g, 8, layout=cr.LAYOUT_ROWMAJOR)
+    del w
+    lb = (torch.randn((E, N, rank), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    la = (torch.randn((E, rank, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    qo = torch.empty(cr.convrot_weight_bytes(E, N, K, 8, cr.LAYOUT_MFMA), dtype=torch.int8, device=dev)
+    so = torch.empty((E, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cr.convrot_requantize_lora(q, s, g, lb, la, alpha, 7, q_out=qo, s_out=so, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    elems = E * N * K
+    nbytes = elems * 2 + E * N * 8 + E * N * rank * 2 + E * rank * K * 2  # codes in and out, scales, factors
+    # fp32 operations per weight the method specifies: rank products and sums, alpha, log2(g) butterfly stages
+    # and the scaling, the dequantising multiply and the add, the division
+    ops = (2 * rank + 1 + int(np.log2(g)) + 1 + 2 + 1) * elems
+    achieved = ops / (ms * 1e-3) / 1e12
+    print(f"bench: {ms * 1e3:.1f} us per conversion", file=sys.stderr, flush=True)
+    line = {
+        "metric": "LoRA patch + random-rounding re-quantisation of quantised weights, GB of int8 weights per second",
+        "value": round(elems / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (weights N(0,0.02) drawn on the GPU with torch's generator, LoRA factors N(0,0.02))",
+        "config": {"workload": f"LoRA rank {rank} on quantised gate/up weights E={E} N={N} K={K} group={g}",
+                   "E": E, "N": N, "K": K, "group": g, "rank": rank},
+        "roofline": {"kernel": "lora_requant_kernel", "bound": "alu", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_VALU_OPS, 1), "unit": "T fp32 ops/s", "frac": round(achieved / PEAK_VALU_OPS, 4),
+                     "traffic": None, "launch_us": round(ms * 1e3, 2),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_experts > 0:
+        import oracle
+        qh, sh = q[:1].cpu().numpy(), s[:1].cpu().numpy()
+        lbh = lb[:1].view(torch.int16).cpu().numpy().view(np.uint16)
+        lah = la[:1].view(torch.int16).cpu().numpy().view(np.uint16)
+        reps, dt = 0, 0.0
+        while reps == 0 or (dt < 10.0 and reps < 64):
+            t0 = time.perf_counter()
+            oracle.requantize_lora(qh, sh, g, lbh, lah, alpha, 7)
+            dt += time.perf_counter() - t0
+            reps += 1
+        line["cpu_baseline"] = {"value": N * K * reps / dt / 1e9, "unit": "GB/s", "cores": cpu_cores(),
+                                "kind": "oracle", "sample": f"expert 0 of the set ({N} x {K}), run {reps} times "
+                                                            f"in {dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,7 +287,7 @@ def main():
     ap.add_argument("--cpu-experts", type=int, default=64,
                     help="experts in the CPU-oracle sample of the MoE workload; 0 skips the CPU baseline (either workload)")
     ap.add_argument("--kernel-iters", type=int, default=50, help="timed launches of the dominant kernel")
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense", "lora"])
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
     args = ap.parse_args()
     if args.gpus != 1:
@@ -213,6 +295,8 @@ def main():
                  "(expert-parallel sharding is described in the design notes, not built)")
     if args.workload == "dense":
         return run_dense(args)
+    if args.workload == "lora":
+        return run_lora(args)
 
     import torch
     from w8a8_rotated_int8_amd import binding as cr

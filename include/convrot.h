@@ -121,6 +121,25 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
 /* Single W8A8 ConvRot linear  (model card "Quantization": W8A8 ConvRot linear with BF16 outputs)          */
 /* ---------------------------------------------------------------------------------------------------- */
 
+/* LoRA patch of quantised weights, re-quantised with random rounding ("NitroFusion2 for ComfyUI", "Why a
+ * step-1 file": a LoRA on a quantised file is re-quantised with fresh scales and random rounding;
+ * "XB_UNetLoaderINTROCm", "Inputs that matter": a stochastic LoRA mode bakes LoRAs in at load).
+ * q_in (device) [E, N, K] int8 row-major codes and s_in (device) [E, N] scales of weights quantised with
+ * `group` (convrot_quantize_weights, CONVROT_LAYOUT_ROWMAJOR, 8 bits); lora_b (device) [E, N, rank] and
+ * lora_a (device) [E, rank, K] bf16, the LoRA factors in the original basis (both may be NULL when rank is 0);
+ * alpha: the LoRA strength; seed: selects the random stream.  Writes q_out (device) in `layout` (int8;
+ * convrot_weight_bytes(E, N, K, 8, layout) bytes) and s_out (device) [E, N].
+ * Per row, in the rotated basis: V = (float)q * s + rotate(alpha * lora_b . lora_a) (delta summed over the
+ * rank in ascending order in fp32, then rotated like the weights); scale = max|V| / 127; t = V / scale;
+ * code = floor(t), plus 1 when u < t - floor(t), clamped to +-127, where u is the top 24 bits (times 2^-24)
+ * of word k % 4 of Philox4x64-10 (Salmon et al., SC 2011) at counter ((e N + n) K/4 + k/4, 0, 0, 0), key
+ * (seed, 0).  Deterministic for a given seed.  Requires E, N >= 1, K <= 8192, K % group == 0, group 64 or
+ * 256, 0 <= rank <= 4096, alpha finite, q_in, lora_a and q_out 16-byte aligned; errors write nothing. */
+convrot_status convrot_requantize_lora(const int8_t* q_in, const float* s_in, int E, int N, int K, int group,
+                                       const uint16_t* lora_b, const uint16_t* lora_a, int rank, float alpha,
+                                       uint64_t seed, int layout, int8_t* q_out, float* s_out,
+                                       hipStream_t stream);
+
 /* Bytes of workspace convrot_linear_w8a8 needs for an [M, K] input. */
 size_t convrot_linear_workspace_bytes(int M, int K);
 

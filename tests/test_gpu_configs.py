@@ -11,7 +11,9 @@ BF16 within 1e-2 relative (and, the arithmetic being fully specified, expected b
     GPU by torch's generator, copied to the host for the oracle);
   * dense W8A8 ConvRot linears over the same T = 8192 tokens (fused qkv, an FFN-down-like [2048, 8192] and the
     attention output projection with group 64 and a bias), through the linear entry point and through its GEMM
-    stage from the oracle's token codes.
+    stage from the oracle's token codes;
+  * a rank-16 LoRA patched onto the 64 quantised down projections [2048, 1536] (group 64) and re-quantised with
+    random rounding, in the layout the GEMM streams.
 """
 import numpy as np
 import pytest
@@ -118,3 +120,19 @@ def test_dense_linear_full_size(name):
     assert exact == 1.0
     y2 = cr.convrot_gemm_w8a8_bf16(dev(rqx), dev(rsx), qw, sw, bias=bd)
     assert np.array_equal(host_bf16(y2), ry), "GEMM stage"
+
+
+def test_lora_requant_full_size_down_weights():
+    E, N, K, g, rank = 64, 2048, 1536, 64, 16
+    say(f"lora requant full size E={E} N={N} K={K} rank={rank}")
+    w = synth.weights(3000 + synth.ROLE_WDN, (E, N, K))
+    q, s = oracle.quantize_weights(w, g, 8)
+    rng = np.random.default_rng(31)
+    lb = synth.to_bf16_bits((rng.standard_normal((E, N, rank)) * 0.02).astype(np.float32))
+    la = synth.to_bf16_bits((rng.standard_normal((E, rank, K)) * 0.02).astype(np.float32))
+    qt, st = cr.convrot_requantize_lora(dev(q), dev(s), g, dev_bf16(lb), dev_bf16(la), 0.5, 2024)
+    torch.cuda.synchronize()
+    say("lora requant: oracle")
+    rq, rs = oracle.requantize_lora(q, s, g, lb, la, 0.5, 2024)
+    assert np.array_equal(host(st).view(np.uint32), rs.view(np.uint32)), "scales"
+    assert np.array_equal(untile_codes(host(qt), E, N, K, 8), rq), "codes"

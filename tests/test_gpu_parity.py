@@ -188,6 +188,40 @@ def test_linear_bit_exact(M, K, N, g, with_bias):
 
 
 # ----------------------------------------------------------------------------------------------------------
+# LoRA patch of quantised weights, re-quantised with random rounding
+# ----------------------------------------------------------------------------------------------------------
+
+def _lora_case(E, N, K, g, rank, seed):
+    rng = np.random.default_rng(seed)
+    w = synth.weights(seed, (E, N, K))
+    q, s = oracle.quantize_weights(w, g, 8)
+    lb = synth.to_bf16_bits((rng.standard_normal((E, N, rank)) * 0.05).astype(np.float32))
+    la = synth.to_bf16_bits((rng.standard_normal((E, rank, K)) * 0.05).astype(np.float32))
+    return q, s, lb, la
+
+
+@pytest.mark.parametrize("E,N,K,g,rank,alpha", [(2, 37, 512, 64, 8, 0.5), (1, 64, 2048, 256, 16, 1.0),
+                                                (3, 5, 256, 64, 0, 1.0), (2, 33, 1536, 64, 4, -0.75),
+                                                (1, 32, 8192, 256, 2, 2.0)])
+def test_lora_requant_bit_exact(E, N, K, g, rank, alpha):
+    say(f"lora requant E={E} N={N} K={K} g={g} rank={rank} alpha={alpha}")
+    q, s, lb, la = _lora_case(E, N, K, g, rank, 900 + N + K)
+    rq, rs = oracle.requantize_lora(q, s, g, lb, la, alpha, seed=77)
+    qd, sd = dev(q), dev(s)
+    lbd = dev_bf16(lb) if rank else None
+    lad = dev_bf16(la) if rank else None
+    q_row, s_row = cr.convrot_requantize_lora(qd, sd, g, lbd, lad, alpha, 77, layout=cr.LAYOUT_ROWMAJOR)
+    assert np.array_equal(host(s_row).view(np.uint32), rs.view(np.uint32)), "scales"
+    assert np.array_equal(host(q_row), rq), "codes (row-major)"
+    q_t, s_t = cr.convrot_requantize_lora(qd, sd, g, lbd, lad, alpha, 77, layout=cr.LAYOUT_MFMA)
+    assert np.array_equal(untile_codes(host(q_t), E, N, K, 8), rq), "codes (MFMA layout)"
+    assert np.array_equal(host(s_t), host(s_row))
+    if rank:  # without a delta the quotients are (nearly always) whole numbers: nothing random to round
+        q_o, _ = cr.convrot_requantize_lora(qd, sd, g, lbd, lad, alpha, 78, layout=cr.LAYOUT_ROWMAJOR)
+        assert not np.array_equal(host(q_o), rq), "another seed draws other roundings"
+
+
+# ----------------------------------------------------------------------------------------------------------
 # Routing
 # ----------------------------------------------------------------------------------------------------------
 

@@ -184,6 +184,25 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
     return CONVROT_OK;
 }
 
+convrot_status convrot_requantize_lora(const int8_t* q_in, const float* s_in, int E, int N, int K, int group,
+                                       const uint16_t* lora_b, const uint16_t* lora_a, int rank, float alpha,
+                                       uint64_t seed, int layout, int8_t* q_out, float* s_out,
+                                       hipStream_t stream) {
+    if (!q_in || !s_in || !q_out || !s_out) return CONVROT_ERR_NULL;
+    if (rank < 0 || rank > 4096) return CONVROT_ERR_SHAPE;
+    if (rank > 0 && (!lora_b || !lora_a)) return CONVROT_ERR_NULL;
+    if (layout != CONVROT_LAYOUT_ROWMAJOR && layout != CONVROT_LAYOUT_MFMA) return CONVROT_ERR_SHAPE;
+    if (E < 1 || N < 1 || K < 1 || K > kMaxRowLen || !std::isfinite(alpha)) return CONVROT_ERR_SHAPE;
+    if ((int64_t)E * ((N + 31) / 32) * 32 > (int64_t)4 * INT32_MAX) return CONVROT_ERR_SHAPE;
+    if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
+    if (!aligned16(q_in) || !aligned16(q_out) || (rank > 0 && !aligned16(lora_a)) ||
+        (reinterpret_cast<uintptr_t>(s_in) & 3) || (reinterpret_cast<uintptr_t>(s_out) & 3) ||
+        (rank > 0 && (reinterpret_cast<uintptr_t>(lora_b) & 1)))
+        return CONVROT_ERR_ALIGN;
+    return hip_status(crk::launch_requantize_lora(q_in, s_in, E, N, K, group, lora_b, lora_a, rank, alpha, seed,
+                                                  layout == CONVROT_LAYOUT_MFMA, q_out, s_out, stream));
+}
+
 size_t convrot_linear_workspace_bytes(int M, int K) {
     if (M < 1 || K < 1) return 0;
     Carver cv(nullptr);

@@ -12,6 +12,10 @@ namespace crk {
 hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
                            hipStream_t st);
 // Weights [E, N, K]: row-major codes, or the MFMA-tiled layout when `tiled` (rows padded to blocks of 32).
+// LoRA patch of row-major int8 weights [E, N, K], re-quantised with random rounding (int8, row-major or tiled)
+hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, int N, int K, int group,
+                                  const uint16_t* lb, const uint16_t* la, int rank, float alpha, uint64_t seed,
+                                  bool tiled, int8_t* qout, float* sout, hipStream_t st);
 hipError_t launch_rotq_weights(const uint16_t* w, int E, int N, int K, int group, int bits, bool tiled, void* q,
                                float* s, hipStream_t st);
 hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,

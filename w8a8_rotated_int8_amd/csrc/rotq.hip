@@ -225,6 +225,160 @@ __global__ __launch_bounds__(256) void rotq_act_split_kernel(const uint16_t* __r
     rotq_fast_part<G, RW, WPR>(x, row, row < rows, K, w % WPR, q, s, xch);
 }
 
+// ---- LoRA patch of quantised weights, re-quantised with random rounding ----------------------------------
+// NitroFusion2 page ("Why a step-1 file"): a LoRA applied to a quantised file is re-quantised with fresh
+// scales and random rounding; XB loader page ("Inputs that matter"): a stochastic LoRA mode bakes LoRAs in at
+// load with random-rounding deltas.  Per row n of expert e, in the rotated basis:
+//   R = (float)q * s;  D[k] = alpha * sum_j B[n, j] * A[j, k] (ascending j from +0, separate mul and add);
+//   V = R + rotate_g(D);  scale = max|V| / 127;  t = V / scale;
+//   code = clamp(floor(t) + (u < t - floor(t)), -127, 127), u = top 24 bits of a Philox4x64-10 word times 2^-24
+//   (counter ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0), word k % 4).
+
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011): each round takes the full 128-bit products of counter words 0 and 2 with the two multipliers;
+// the key advances by the two Weyl constants before every round but the first.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+    constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+    constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += kW0;
+            k1 += kW1;
+        }
+        const uint64_t lo0 = kM0 * c[0], hi0 = __umul64hi(kM0, c[0]);
+        const uint64_t lo1 = kM1 * c[2], hi1 = __umul64hi(kM1, c[2]);
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+// One wavefront per row (rows in the launch order of rotq_rows_kernel: tiled modes include the padding rows of
+// the last 32-row block, which get zero codes).  Lane l holds the vectors i = l + 64 j (elements 8i .. 8i+7).
+template <int G, int NV, Out OUT>
+__global__ __launch_bounds__(256) void lora_requant_kernel(const int8_t* __restrict__ qin, const float* __restrict__ sin,
+                                                           int64_t rows, int K, int N,
+                                                           const uint16_t* __restrict__ lb,
+                                                           const uint16_t* __restrict__ la, int rank, float alpha,
+                                                           uint64_t seed, int8_t* __restrict__ qout,
+                                                           float* __restrict__ sout) {
+    constexpr bool kTiled = OUT == Out::kTiledI8;
+    const int lane = threadIdx.x & 63;
+    const int64_t lrow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int64_t row = lrow, expert = 0;
+    int n = 0;
+    bool pad = false;
+    if constexpr (kTiled) {
+        const int nbr = ((N + 31) >> 5) << 5;
+        expert = lrow / nbr;
+        n = (int)(lrow - expert * nbr);
+        if (expert * N >= rows) return;  // wave-uniform
+        pad = n >= N;
+        row = expert * N + n;
+    } else {
+        if (row >= rows) return;  // wave-uniform
+        expert = row / N;
+    }
+    const int nvec = K >> 3;
+
+    // delta row, then rotated
+    Vec8 d[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[j].v[e] = 0.0f;
+    if (!pad) {
+        for (int r = 0; r < rank; ++r) {
+            const float b = bf16_to_float(lb[row * rank + r]);
+            const uint16_t* arow = la + (expert * rank + r) * (int64_t)K;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int i = lane + 64 * j;
+                if (i >= nvec) continue;
+                const uint4 raw = *reinterpret_cast<const uint4*>(arow + 8 * i);
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = b * bf16_to_float(w[e] & 0xffffu);
+                    const float p1 = b * bf16_to_float(w[e] >> 16);
+                    d[j].v[2 * e] = d[j].v[2 * e] + p0;
+                    d[j].v[2 * e + 1] = d[j].v[2 * e + 1] + p1;
+                }
+            }
+        }
+    }
+    constexpr float kNorm = (G == 256) ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[j].v[e] = alpha * d[j].v[e];
+        fwht_vec_inlane<G>(d[j]);
+        fwht_vec_crosslane<G>(d[j], lane);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[j].v[e] = d[j].v[e] * kNorm;
+    }
+
+    // patched rotated row and its maximum
+    const float s0 = pad ? 0.0f : sin[row];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        int8_t c8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (i < nvec && !pad) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(qin + row * (int64_t)K + 8 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c8[e] = (int8_t)(raw.x >> (8 * e));
+                c8[4 + e] = (int8_t)(raw.y >> (8 * e));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = (float)c8[e] * s0;
+            d[j].v[e] = (i < nvec) ? r + d[j].v[e] : 0.0f;
+            amax = fmaxf(amax, fabsf(d[j].v[e]));
+        }
+    }
+    amax = wave_max(amax);
+    const float scale = amax / 127.0f;
+
+    const int64_t flat0 = row * (int64_t)(K / 4);  // Philox counter of this row's first 4 elements
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i >= nvec) continue;
+        int c[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint64_t ctr[4] = {(uint64_t)(flat0 + 2 * i + h), 0, 0, 0};
+            philox4x64_10(ctr, seed, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float u = (float)(ctr[e] >> 40) * 0x1p-24f;
+                float code = 0.0f;
+                if (scale != 0.0f) {
+                    const float t = d[j].v[4 * h + e] / scale;
+                    const float fl = floorf(t);
+                    code = fl + (u < t - fl ? 1.0f : 0.0f);
+                    code = fminf(fmaxf(code, -127.0f), 127.0f);
+                }
+                c[4 * h + e] = pad ? 0 : (int)code;
+            }
+        }
+        uint2 o;
+        o.x = pack4_i8(c[0], c[1], c[2], c[3]);
+        o.y = pack4_i8(c[4], c[5], c[6], c[7]);
+        const int64_t off = kTiled ? expert * (int64_t)(((N + 31) >> 5) << 5) * K + tiled_offset<false>(n, 8 * i, K)
+                                   : row * (int64_t)K + 8 * i;
+        *reinterpret_cast<uint2*>(qout + off) = o;
+    }
+    if (lane == 0 && !pad) sout[row] = scale;
+}
+
 // rows: source rows (E * N for weights); N: rows per expert (tiled modes only).
 template <int G, int QMAX, Out OUT, bool CHECK>
 hipError_t launch_nv(const void* x, int64_t rows, int K, int N, void* q, float* s, float* rot, hipStream_t st) {
@@ -282,6 +436,36 @@ hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, in
     }
     if (group == 256) return launch_nv<256, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
     return launch_nv<64, 127, Out::kRowI8, false>(x, rows, K, 0, q, s, rot, st);
+}
+
+hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, int N, int K, int group,
+                                  const uint16_t* lb, const uint16_t* la, int rank, float alpha, uint64_t seed,
+                                  bool tiled, int8_t* qout, float* sout, hipStream_t st) {
+    const int64_t rows = (int64_t)E * N;
+    if (rows == 0) return hipSuccess;
+    const int nv = (K / 8 + 63) / 64;
+    const int64_t launch_rows = tiled ? (int64_t)E * (((N + 31) >> 5) << 5) : rows;
+    const dim3 grid((unsigned)((launch_rows + 3) / 4)), block(256);
+#define CRK_LR(GG, NVC)                                                                                       \
+    if (group == GG && nv <= NVC) {                                                                           \
+        if (tiled)                                                                                            \
+            lora_requant_kernel<GG, NVC, Out::kTiledI8><<<grid, block, 0, st>>>(qin, sin, rows, K, N, lb, la, \
+                                                                                 rank, alpha, seed, qout, sout);\
+        else                                                                                                  \
+            lora_requant_kernel<GG, NVC, Out::kRowI8><<<grid, block, 0, st>>>(qin, sin, rows, K, N, lb, la,   \
+                                                                               rank, alpha, seed, qout, sout);  \
+        return hipGetLastError();                                                                             \
+    }
+    CRK_LR(256, 4)
+    CRK_LR(256, 8)
+    CRK_LR(256, 16)
+    CRK_LR(64, 1)
+    CRK_LR(64, 2)
+    CRK_LR(64, 4)
+    CRK_LR(64, 8)
+    CRK_LR(64, 16)
+#undef CRK_LR
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_rotq_weights(const uint16_t* w, int E, int N, int K, int group, int bits, bool tiled, void* q,
