@@ -51,7 +51,7 @@
  *    rounding floor(t) + [u < t - floor(t)] with u uniform in [0, 1) from Philox4x64-10 (a counter-based
  *    generator, see oracle_philox4x64_10): counter ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0), word
  *    k % 4, top 24 bits times 2^-24.  Delta sums in ascending rank index from +0.0f, separate multiply and
- *    add, then times alpha.  The pages fix none of these details; parity pinned by the tests below.
+ *    add, then times alpha.  The pages fix none of these details (pinned by the oracle-pin tests).
  */
 #include <math.h>
 #include <stdint.h>
