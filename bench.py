@@ -282,7 +282,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3], help="2: T=2048 C=64; 3: T=8192 C=256")
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4],
+                    help="2: T=2048 C=64; 3: T=8192 C=256; 4: the T=8192 layer stacked --layers times, each layer "
+                         "with its own weights and logits (weights drawn on the GPU), a step being the whole stack")
+    ap.add_argument("--layers", type=int, default=29, help="layers of the config-4 stack")
     ap.add_argument("--wbits", type=int, default=8, choices=[8, 4])
     ap.add_argument("--cpu-experts", type=int, default=64,
                     help="experts in the CPU-oracle sample of the MoE workload; 0 skips the CPU baseline (either workload)")
@@ -304,15 +307,37 @@ def main():
 
     dev = torch.device("cuda:0")
     s = synth.CONFIGS[args.config]
-    print(f"bench: config {args.config} T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} wbits={args.wbits}", file=sys.stderr,
-          flush=True)
-    x, lg, w_gu, w_dn = synth.moe_inputs(args.config)
+    n_layers = args.layers if args.config == 4 else 1
+    print(f"bench: config {args.config} T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} wbits={args.wbits} "
+          f"layers={n_layers}", file=sys.stderr, flush=True)
 
     def bf16_dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    xd, lgd = bf16_dev(x), torch.from_numpy(lg).to(dev)
-    w = cr.quantize_moe_weights(bf16_dev(w_gu), bf16_dev(w_dn), s.g_gu, s.g_dn, args.wbits)
+    def host_bf16(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    # layers: (router logits on the device, converted weights); the CPU sample takes layer 0's first experts
+    layers = []
+    if args.config == 4:
+        if n_layers < 1:
+            sys.exit("bench.py: --layers must be at least 1")
+        x = synth.stack_x(s)
+        for li in range(n_layers):
+            lgd_l, w_gu_d, w_dn_d = synth.stack_layer_device(li, s, dev)
+            if li == 0:
+                lg = lgd_l.cpu().numpy()
+                n_cpu = max(args.cpu_experts, 1)
+                w_gu, w_dn = host_bf16(w_gu_d[:n_cpu]), host_bf16(w_dn_d[:n_cpu])
+            layers.append((lgd_l, cr.quantize_moe_weights(w_gu_d, w_dn_d, s.g_gu, s.g_dn, args.wbits)))
+            del w_gu_d, w_dn_d
+        print(f"bench: {n_layers} layers converted", file=sys.stderr, flush=True)
+    else:
+        x, lg, w_gu, w_dn = synth.moe_inputs(args.config)
+        layers.append((torch.from_numpy(lg).to(dev),
+                       cr.quantize_moe_weights(bf16_dev(w_gu), bf16_dev(w_dn), s.g_gu, s.g_dn, args.wbits)))
+    xd = bf16_dev(x)
+    w = layers[0][1]
     out = torch.empty((s.T, s.d), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((s.E, s.C), dtype=torch.int32, device=dev)
     wt = torch.empty((s.E, s.C), dtype=torch.float32, device=dev)
@@ -320,7 +345,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        cr.moe_expert_choice_forward(xd, lgd, s.C, w, out=out, idx_out=idx, wt_out=wt, ws=ws, stream=stream)
+        for lgd_l, w_l in layers:
+            cr.moe_expert_choice_forward(xd, lgd_l, s.C, w_l, out=out, idx_out=idx, wt_out=wt, ws=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -338,15 +364,16 @@ def main():
           file=sys.stderr, flush=True)
 
     # Dominant kernel: the grouped gate/up GEMM, timed on its own stage entry point (same kernel, same inputs,
-    # the routing of the last step) with HIP events on the stream it is launched on.
+    # the routing of the last step) with HIP events on the stream it is launched on.  In the stack, successive
+    # launches take successive layers' weights, so each launch streams weights the previous ones did not touch.
     qx, sx, _ = cr.convrot_rotq_rows(xd, s.g_gu)
     a = torch.empty((s.E * s.C, s.I), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        cr.moe_gateup_swiglu(qx, sx, idx, w, a_out=a, stream=stream)
+    for i in range(3):
+        cr.moe_gateup_swiglu(qx, sx, idx, layers[i % n_layers][1], a_out=a, stream=stream)
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
-    for _ in range(args.kernel_iters):
-        cr.moe_gateup_swiglu(qx, sx, idx, w, a_out=a, stream=stream)
+    for i in range(args.kernel_iters):
+        cr.moe_gateup_swiglu(qx, sx, idx, layers[i % n_layers][1], a_out=a, stream=stream)
     k1.record(stream)
     torch.cuda.synchronize()
     k_us = k0.elapsed_time(k1) / args.kernel_iters * 1e3
@@ -356,8 +383,14 @@ def main():
     print(f"bench: gate/up GEMM {k_us:.1f} us/launch, {achieved:.0f} GB/s algorithmic, {gemm_tops:.0f} TOPS",
           file=sys.stderr, flush=True)
 
-    sec = ms * 1e-3
+    sec = ms * 1e-3 / n_layers  # one layer
     tops = layer_ops(s) / sec / 1e12
+    workload = (f"expert-choice W8A8 ConvRot MoE layer T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} "
+                f"(g_gu={s.g_gu}, g_dn={s.g_dn}, {args.wbits}-bit weights)")
+    if n_layers > 1:
+        workload = f"{n_layers} stacked {workload.replace('layer', 'layers', 1)}, each with its own weights and logits"
+    # the committed counter summary covers the 8-bit gate/up launch at T=8192, C=256
+    traffic = read_traffic() if (s.T, s.C, args.wbits) == (8192, 256, 8) else None
     line = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -372,15 +405,15 @@ def main():
         "dtype": "int8" if args.wbits == 8 else "int4w-int8a",
         "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x20, N(0,0.02) weights, "
                 "N(0,1) router logits)",
-        "config": {"workload": f"expert-choice W8A8 ConvRot MoE layer T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} "
-                               f"(g_gu={s.g_gu}, g_dn={s.g_dn}, {args.wbits}-bit weights)",
-                   "T": s.T, "d": s.d, "E": s.E, "I": s.I, "C": s.C, "wbits": args.wbits},
+        "config": {"workload": workload, "T": s.T, "d": s.d, "E": s.E, "I": s.I, "C": s.C, "wbits": args.wbits,
+                   "layers": n_layers},
+        "us_per_layer": round(sec * 1e6, 2),
         "tokens_per_s": round(s.T / sec, 1),
         "frac_int8_mfma_peak": round(tops / PEAK_INT8_TOPS, 4),
         "frac_hbm_peak": round(layer_bytes(s, args.wbits) / sec / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": {"kernel": "grouped gate/up INT8 GEMM + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": read_traffic(), "launch_us": round(k_us, 2),
+                     "traffic": traffic, "launch_us": round(k_us, 2),
                      "mfma_frac": round(gemm_tops / PEAK_INT8_TOPS, 4)},
         "cpu_baseline": None,
     }
