@@ -10,7 +10,7 @@ tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection).  -
 LoRA patch of the layer's quantised gate/up weights (64 x [3072, 2048], rank 32), re-quantised with random
 rounding into the layout the GEMM streams.
 
-Prints one JSON line (see --help for options).  --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line (see --help for options).  --gpus above 1 is refused: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -294,8 +294,8 @@ def main():
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
     args = ap.parse_args()
     if args.gpus != 1:
-        sys.exit(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-                 "(expert-parallel sharding is described in the design notes, not built)")
+        sys.exit(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported "
+                 "(sharding the experts over several GPUs is not built)")
     if args.workload == "dense":
         return run_dense(args)
     if args.workload == "lora":
