@@ -42,6 +42,9 @@ __device__ __forceinline__ float swz_xor4(float v) {
 __device__ __forceinline__ uint32_t code_bits(float t) {
     return __float_as_uint(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f) + 12582912.0f);
 }
+// The same for |t| < 127.5, with no clamp.  The fast path's quotients are in range: |v| <= amax and
+// sc = amax / 127 rounded to nearest, so |v / sc| <= 127 / (1 - 2^-24) < 127.00001.
+__device__ __forceinline__ uint32_t code_bits_in_range(float t) { return __float_as_uint(t + 12582912.0f); }
 // Low bytes of four such words, packed in order.
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // bytes: a0, b0, 0, 0
@@ -134,7 +137,7 @@ __device__ __forceinline__ void rotq_fast_part(const uint16_t* __restrict__ x, i
                 for (int u = 0; u < 4; ++u) {
                     const float q0 = v[r][e + u] * y;
                     const float rem = __builtin_fmaf(-q0, sc, v[r][e + u]);
-                    b[u] = code_bits(__builtin_fmaf(rem, y, q0));
+                    b[u] = code_bits_in_range(__builtin_fmaf(rem, y, q0));
                 }
                 packed[e / 4] = pack4(b[0], b[1], b[2], b[3]);
             }
