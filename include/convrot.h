@@ -37,7 +37,9 @@
  * Conventions for every call:
  *  - Pointers marked (device) are device memory on the current HIP device; bf16 crosses the ABI as raw
  *    uint16_t bits.  The caller owns every buffer; the library allocates nothing and keeps no state between
- *    calls, so calls are thread-safe.  Calls only enqueue work on `stream` (0 = the null stream) and return.
+ *    calls beyond what it sets up once (each GEMM kernel's LDS size attribute, and a per-device count of
+ *    compute units held in an atomic), so calls are thread-safe.
+ *    Calls only enqueue work on `stream` (0 = the null stream) and return.
  *  - Arguments are validated on the host before anything is enqueued; on an error nothing is written.
  *    CONVROT_ERR_HIP means a launch failed after validation; outputs are then unspecified.
  *  - Row strides equal the row length (dense row-major).  Every device pointer must be 16-byte aligned.

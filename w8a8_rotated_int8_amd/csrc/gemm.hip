@@ -41,6 +41,7 @@
 //     matrix pipe never waits for a whole stage of fragment reads.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -673,16 +674,17 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
     if (total > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t ldo = (EPI == Epi::kSwiGLU) ? p.N / 2 : p.N;
     if ((int64_t)BM * ldo * 2 >= kOobOffset) return hipErrorInvalidValue;  // an output tile must fit one range
-    static int ncu_cache[64] = {0};
+    // compute units per device, looked up once (calls from several threads may race to store the same value)
+    static std::atomic<int> ncu_cache[64];
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    int ncu = (dev >= 0 && dev < 64) ? ncu_cache[dev] : 0;
+    int ncu = (dev >= 0 && dev < 64) ? ncu_cache[dev].load(std::memory_order_relaxed) : 0;
     if (ncu <= 0) {
         err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
         if (ncu <= 0) return hipErrorInvalidValue;
-        if (dev >= 0 && dev < 64) ncu_cache[dev] = ncu;
+        if (dev >= 0 && dev < 64) ncu_cache[dev].store(ncu, std::memory_order_relaxed);
     }
     const int grid = (int)(total < ncu ? total : ncu);  // one persistent workgroup per CU
     kern<<<dim3((unsigned)grid), dim3(kThreads), Cfg::LDS, st>>>(p, tiles_m, tiles_n);
