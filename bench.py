@@ -115,6 +115,19 @@ def dense_cpu_baseline(x, q, s, g, b, M, K, N, min_seconds: float = 10.0):
             "sample": f"the whole linear (M={M}, K={K}, N={N}), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s"}
 
 
+def add_measured_peaks(line, stream, mfma_tops=None, hbm_gbs=None):
+    """What the chip sustains (the library's probes, timed in this run), beside the datasheet peaks the roofline
+    uses: the dominant kernel's rate as a fraction of each."""
+    from w8a8_rotated_int8_amd import profiling
+    pk = profiling.measured_peaks(stream)
+    print(f"bench: measured peaks {pk}", file=sys.stderr, flush=True)
+    line["measured_peaks"] = pk
+    if mfma_tops is not None:
+        line["roofline"]["frac_of_measured_int8_mfma_random"] = round(mfma_tops / pk["int8_mfma_random_tops"], 4)
+    if hbm_gbs is not None:
+        line["roofline"]["frac_of_measured_hbm_read"] = round(hbm_gbs / pk["hbm_read_gbs"], 4)
+
+
 def run_dense(args):
     import torch
     from w8a8_rotated_int8_amd import binding as cr
@@ -189,6 +202,8 @@ def run_dense(args):
                      "hbm_frac": round(gemm_bytes / (k_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
     }
+    if args.peaks:
+        add_measured_peaks(line, stream, mfma_tops=gemm_tops)
     if args.cpu_experts > 0:
         import oracle
         q, s = oracle.quantize_weights(w, g, 8)
@@ -291,6 +306,8 @@ def main():
                     help="experts in the CPU-oracle sample of the MoE workload; 0 skips the CPU baseline (either workload)")
     ap.add_argument("--kernel-iters", type=int, default=50, help="timed launches of the dominant kernel")
     ap.add_argument("--workload", default="moe", choices=["moe", "dense", "lora"])
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the achievable-rate probes (int8 MFMA, HBM read) reported beside the roofline")
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
     args = ap.parse_args()
     if args.gpus != 1:
@@ -417,6 +434,8 @@ def main():
                      "mfma_frac": round(gemm_tops / PEAK_INT8_TOPS, 4)},
         "cpu_baseline": None,
     }
+    if args.peaks:
+        add_measured_peaks(line, stream, mfma_tops=gemm_tops, hbm_gbs=achieved)
     if args.cpu_experts > 0:
         print(f"bench: timing the CPU oracle on {args.cpu_experts} experts", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x, lg, w_gu, w_dn, s, args.cpu_experts)

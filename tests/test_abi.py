@@ -1,5 +1,6 @@
-"""The C ABI on the host, no GPU needed: the library loads, exports every function include/convrot.h declares,
-and rejects invalid arguments (validation runs before anything touches the GPU)."""
+"""The C ABI on the host, no GPU needed: the library loads, exports every function include/convrot.h and
+include/convrot_probes.h declare, and rejects invalid arguments (validation runs before anything touches the
+GPU)."""
 import ctypes
 
 import pytest
@@ -17,10 +18,17 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
+
+
+def test_probe_validation(L):
+    d = ctypes.c_double(0.0)
+    assert L.convrot_probe_mfma_i8(None, 1 << 18, 1, P, 1 << 20, ctypes.byref(d), None) == NULL
+    assert L.convrot_probe_mfma_i8(P, 1 << 18, 1, P, 1 << 20, None, None) == NULL
+    assert L.convrot_probe_hbm_read(P, 1 << 30, None, 1 << 20, ctypes.byref(d), None) == NULL
 
 
 def test_status_strings(L):

@@ -19,6 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libconvrot_amd.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "convrot.h")
+PROBES_HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "convrot_probes.h")
 
 STATUS = {0: "CONVROT_OK", 1: "CONVROT_ERR_NULL", 2: "CONVROT_ERR_SHAPE", 3: "CONVROT_ERR_GROUP",
           4: "CONVROT_ERR_BITS", 5: "CONVROT_ERR_ALIGN", 6: "CONVROT_ERR_WORKSPACE", 7: "CONVROT_ERR_NONFINITE",
@@ -58,6 +59,9 @@ _SIGS = {
     "moe_down_proj": (_i, [_p, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p]),
     "moe_combine_workspace_bytes": (_sz, [_i, _i]),
     "moe_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "convrot_probe_out_words": (_sz, []),
+    "convrot_probe_mfma_i8": (_i, [_p, _sz, _i, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
+    "convrot_probe_hbm_read": (_i, [_p, _sz, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
 }
 
 _lock = threading.Lock()
@@ -82,8 +86,8 @@ def lib():
 
 
 def header_functions() -> list[str]:
-    """Names of the functions declared in include/convrot.h."""
-    text = open(HEADER_PATH).read()
+    """Names of the functions declared in include/convrot.h and include/convrot_probes.h."""
+    text = open(HEADER_PATH).read() + open(PROBES_HEADER_PATH).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\(", text, flags=re.M)))
 
 
@@ -284,6 +288,25 @@ def convrot_gemm_w8a8_bf16(qx, sx, qw, sw, bias=None, y=None, stream=None):
     _check("convrot_gemm_w8a8_bf16", lib().convrot_gemm_w8a8_bf16(
         _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y), _stream(stream)))
     return y
+
+
+def convrot_probe_mfma_i8(src, iters: int, out, stream=None) -> float:
+    """Enqueue the int8 MFMA rate probe (src: >= 256 KiB int8 operand pool; out: convrot_probe_out_words()
+    int32); returns the int8 operations the launch performs."""
+    ops = ctypes.c_double(0.0)
+    _check("convrot_probe_mfma_i8", lib().convrot_probe_mfma_i8(
+        _ptr(src), src.numel() * src.element_size(), iters, _ptr(out), out.numel(), ctypes.byref(ops),
+        _stream(stream)))
+    return ops.value
+
+
+def convrot_probe_hbm_read(src, out, stream=None) -> float:
+    """Enqueue the HBM read probe over src (device bytes); returns the bytes the launch reads."""
+    nbytes = ctypes.c_double(0.0)
+    _check("convrot_probe_hbm_read", lib().convrot_probe_hbm_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(out), out.numel(), ctypes.byref(nbytes),
+        _stream(stream)))
+    return nbytes.value
 
 
 def convrot_gemm_i8_i32(a, b, acc_out=None, stream=None):

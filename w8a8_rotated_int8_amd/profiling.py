@@ -2,7 +2,9 @@
 
 Used by hand after a profiled run of ``bench.py``; reads only rocprofv3's CSV output (``--output-format csv
 -o run``) and writes short text summaries.  Nothing here runs a kernel except ``copy_probe``, the plain
-device-to-device copy of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters.
+device-to-device copy of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters, and
+``measured_peaks``, which times the library's achievable-rate probes (int8 MFMA on random and on constant
+operands, HBM read through LDS DMA) for ``bench.py``.
 
     python -m w8a8_rotated_int8_amd.profiling stats <run_dir> <out.txt> "<command>"
     python -m w8a8_rotated_int8_amd.profiling copy <MiB> <iters>
@@ -48,6 +50,42 @@ def stats_summary(run_dir: str, out_txt: str, command: str) -> None:
     with open(out_txt, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def measured_peaks(stream=None, mfma_iters: int = 4096, hbm_bytes: int = 4 << 30) -> dict:
+    """What the chip sustains, measured with the library's probes on the current device (best of 3 timed
+    launches each, HIP events on `stream`): int8 MFMA TOPS on random and on constant operand bytes, and HBM
+    read GB/s through non-temporal LDS DMA over `hbm_bytes` (well above the 256 MB memory-side cache)."""
+    import torch
+    from . import binding as cr
+    dev = torch.device("cuda")
+    st = stream or torch.cuda.current_stream()
+    out = torch.empty(cr.lib().convrot_probe_out_words(), dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    pool_rand = torch.randint(-128, 128, (256 * 1024,), dtype=torch.int8, device=dev, generator=g)
+    pool_const = torch.full((256 * 1024,), 0x11, dtype=torch.int8, device=dev)
+    src = torch.empty(hbm_bytes, dtype=torch.int8, device=dev)
+
+    def best(fn):
+        fn()
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            work = fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        return work / min(times)
+
+    res = {
+        "int8_mfma_random_tops": best(lambda: cr.convrot_probe_mfma_i8(pool_rand, mfma_iters, out, st)) / 1e12,
+        "int8_mfma_const_tops": best(lambda: cr.convrot_probe_mfma_i8(pool_const, mfma_iters, out, st)) / 1e12,
+        "hbm_read_gbs": best(lambda: cr.convrot_probe_hbm_read(src, out, st)) / 1e9,
+    }
+    del src
+    return {k: round(v, 1) for k, v in res.items()}
 
 
 def counter_per_dispatch(run_dir: str, counter: str, pattern: str, skip: int = 1):
