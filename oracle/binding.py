@@ -16,6 +16,8 @@ __all__ = [
     "quantize_rows", "rotq_rows", "pack_int4", "unpack_int4", "quantize_weights", "gemm_i8_i32",
     "dequant_bf16", "linear_w8a8", "softmax_experts", "route_from_probs", "route", "swiglu", "combine",
     "moe_gateup", "moe_down", "moe_forward", "moe_rows", "philox4x64_10", "requantize_lora",
+    "e4m3_encode", "e4m3_decode", "pack_int6", "unpack_int6", "quantize_g16", "unpack_g16", "gemm_g16",
+    "linear_g16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +83,13 @@ def _declare(lib):
         "oracle_moe_forward": (_i, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _i,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
         "oracle_moe_rows": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _p, _p, _p, _p, _i, _i, _p, _i, _p]),
+        "oracle_e4m3_encode_array": (None, [_p, _i64, _p]),
+        "oracle_e4m3_decode_array": (None, [_p, _i64, _p]),
+        "oracle_pack_int6": (None, [_p, _i64, _i, _p]),
+        "oracle_unpack_int6": (None, [_p, _i64, _i, _p]),
+        "oracle_quantize_g16_rows": (None, [_p, _i64, _i, _i, _p, _p, _p]),
+        "oracle_quantize_g16": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p]),
+        "oracle_gemm_g16": (None, [_p, _p, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -266,6 +275,89 @@ def linear_w8a8(x, qw, sw, g: int, bias=None):
     _check(load().oracle_linear_w8a8(_ptr(x), M, K, _ptr(qw), _ptr(sw), N, g, _ptr(bias), _ptr(y),
                                      _ptr(qx), _ptr(sx)), "linear")
     return y, qx, sx
+
+
+# --------------------------------------------------------------------------------------------------
+# W6A8 / W4A8 with FP8 (E4M3) group-16 scales
+# --------------------------------------------------------------------------------------------------
+
+def e4m3_encode(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    load().oracle_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(b) -> np.ndarray:
+    b = _c(b, np.uint8)
+    out = np.empty(b.shape, np.float32)
+    load().oracle_e4m3_decode_array(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def pack_int6(q) -> np.ndarray:
+    q = _c(q, np.int8)
+    rows, K = q.shape
+    out = np.empty((rows, K // 4 * 3), np.uint8)
+    load().oracle_pack_int6(_ptr(q), rows, K, _ptr(out))
+    return out
+
+
+def unpack_int6(p, K: int) -> np.ndarray:
+    p = _c(p, np.uint8)
+    rows = p.shape[0]
+    q = np.empty((rows, K), np.int8)
+    load().oracle_unpack_int6(_ptr(p), rows, K, _ptr(q))
+    return q
+
+
+def quantize_g16(w, g: int, bits: int):
+    """w: bf16 bits [N, K].  Returns (packed codes u8 [N, K*bits/8], E4M3 group scales u8 [N, K/16],
+    row scales fp32 [N], codes int8 [N, K])."""
+    w = _c(w, np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K * bits // 8), np.uint8)
+    f8 = np.empty((N, K // 16), np.uint8)
+    s = np.empty(N, np.float32)
+    codes = np.empty((N, K), np.int8)
+    _check(load().oracle_quantize_g16(_ptr(w), N, K, g, bits, _ptr(q), _ptr(f8), _ptr(s), _ptr(codes)),
+           "quantize_g16")
+    return q, f8, s, codes
+
+
+def unpack_g16(q, K: int, bits: int) -> np.ndarray:
+    """Codes int8 [N, K] from the 6- or 4-bit packing."""
+    if bits == 6:
+        return unpack_int6(q, K)
+    return unpack_int4(q, K)
+
+
+def gemm_g16(qx, sx, codes, f8, s_row, bias=None):
+    """Returns (y bf16 bits [M, N], A fp64 [M, N] (exact), sum of |terms| fp64 [M, N])."""
+    qx = _c(qx, np.int8)
+    sx = _c(sx, np.float32)
+    codes = _c(codes, np.int8)
+    f8 = _c(f8, np.uint8)
+    s_row = _c(s_row, np.float32)
+    bias = None if bias is None else _c(bias, np.uint16)
+    M, K = qx.shape
+    N = codes.shape[0]
+    y = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    aabs = np.empty((M, N), np.float64)
+    load().oracle_gemm_g16(_ptr(qx), _ptr(sx), M, K, _ptr(codes), _ptr(f8), _ptr(s_row), N, _ptr(bias), _ptr(y),
+                           _ptr(acc), _ptr(aabs))
+    return y, acc, aabs
+
+
+def linear_g16(x, g: int, codes, f8, s_row, bias=None):
+    """The W6A8 / W4A8 linear: tokens rotated and quantised to int8 per token (as W8A8), then gemm_g16.
+    Returns (y, qx, sx, A, sum of |terms|)."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    qx, sx = rotq_rows(x, g, 127)[:2]
+    y, acc, aabs = gemm_g16(qx, sx, codes, f8, s_row, bias)
+    return y, qx, sx, acc, aabs
 
 
 # --------------------------------------------------------------------------------------------------

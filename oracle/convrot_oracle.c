@@ -52,6 +52,14 @@
  *    generator, see oracle_philox4x64_10): counter ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0), word
  *    k % 4, top 24 bits times 2^-24.  Delta sums in ascending rank index from +0.0f, separate multiply and
  *    add, then times alpha.  The pages fix none of these details (pinned by the oracle-pin tests).
+ *  - W6A8 / W4A8 with an FP8 scale per group of 16 ([NF2] "How they were made"; oracle_quantize_g16,
+ *    oracle_linear_g16): the same block rotation; symmetric integer codes, qmax = 31 (6 bits) or 7 (4 bits);
+ *    FP8 = E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite 448),
+ *    one per group of 16 consecutive k, relative to one fp32 scale per row: s_row = amax / (qmax * 448),
+ *    f_j = E4M3((amax_j / amax) * 448) nearest-even, the group's scale S_j = s_row * f_j, and
+ *    code = clamp(rint(r / S_j), +-qmax) (0 where S_j = 0).  The kernel decodes code * f_j (exact in fp16)
+ *    and multiplies by the row scale after the sum.  Packing: 4-bit as INT4 above; 6-bit codes four to
+ *    three bytes, code 4j+i in bits 6i..6i+5 of the little-endian 24-bit word j.
  */
 #include <math.h>
 #include <stdint.h>
@@ -425,6 +433,165 @@ int oracle_linear_w8a8(const uint16_t* x, int M, int K, const int8_t* qw, const 
     free(sx);
     free(acc);
     return st;
+}
+
+/* ------------------------------------------------------------------------------------------------- */
+/* W6A8 / W4A8: 6- or 4-bit codes with an FP8 (E4M3) scale per group of 16  [NF2]                        */
+/* ------------------------------------------------------------------------------------------------- */
+
+/* E4M3 byte -> value: sign bit 7, exponent bits 3-6 (bias 7), mantissa bits 0-2; exponent field 0 holds
+ * the subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN (no infinities). */
+float oracle_e4m3_decode(uint8_t b) {
+    int e = (b >> 3) & 15, m = b & 7;
+    float v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexpf((float)m, -9);
+    else
+        v = ldexpf((float)(8 + m), e - 10);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Non-negative fp32 -> E4M3 byte: the nearest E4M3 value, ties to the even mantissa; 448 and above give
+ * 448 (0x7e); zero and values below half the smallest subnormal give 0. */
+uint8_t oracle_e4m3_encode(float x) {
+    if (!(x > 0.0f)) return 0;
+    if (x >= 448.0f) return 0x7e;
+    int e2;
+    frexpf(x, &e2); /* x in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < -6) E = -6; /* below 2^-6 the spacing stays 2^-9 (subnormals) */
+    float steps = rintf(ldexpf(x, 3 - E)); /* x in units of the spacing 2^(E-3), exact before rounding */
+    int n = (int)steps;
+    if (E == -6 && n < 8) return (uint8_t)n; /* subnormal or zero */
+    if (n == 16) {                           /* rounded up into the next binade */
+        E += 1;
+        n = 8;
+    }
+    return (uint8_t)(((E + 7) << 3) | (n - 8));
+}
+
+void oracle_e4m3_encode_array(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t* b, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(b[i]);
+}
+
+/* 6-bit packing: codes 4j..4j+3 of a row in bytes 3j..3j+2, code 4j+i in bits 6i..6i+5 (two's complement)
+ * of the little-endian 24-bit word. */
+void oracle_pack_int6(const int8_t* q, int64_t rows, int K, uint8_t* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < K / 4; ++j) {
+            uint32_t w = 0;
+            for (int i = 0; i < 4; ++i) w |= ((uint32_t)(uint8_t)q[r * (int64_t)K + 4 * j + i] & 63u) << (6 * i);
+            uint8_t* o = out + r * (int64_t)(K / 4 * 3) + 3 * j;
+            o[0] = (uint8_t)w;
+            o[1] = (uint8_t)(w >> 8);
+            o[2] = (uint8_t)(w >> 16);
+        }
+}
+
+void oracle_unpack_int6(const uint8_t* p, int64_t rows, int K, int8_t* q) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < K / 4; ++j) {
+            const uint8_t* b = p + r * (int64_t)(K / 4 * 3) + 3 * j;
+            uint32_t w = (uint32_t)b[0] | ((uint32_t)b[1] << 8) | ((uint32_t)b[2] << 16);
+            for (int i = 0; i < 4; ++i) {
+                int c = (int)((w >> (6 * i)) & 63u);
+                q[r * (int64_t)K + 4 * j + i] = (int8_t)(c >= 32 ? c - 64 : c);
+            }
+        }
+}
+
+/* Group-16 quantiser of rotated rows r [rows, K] (K a multiple of 16): codes q (int8 holding the 6- or
+ * 4-bit values), E4M3 group scales f8 [rows, K/16], row scales s_row [rows]. */
+void oracle_quantize_g16_rows(const float* r, int64_t rows, int K, int qmax, int8_t* q, uint8_t* f8,
+                              float* s_row) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float* v = r + i * (int64_t)K;
+        float amax = 0.0f;
+        for (int k = 0; k < K; ++k)
+            if (fabsf(v[k]) > amax) amax = fabsf(v[k]);
+        const float sr = amax / (float)(qmax * 448);
+        s_row[i] = sr;
+        for (int j = 0; j < K / 16; ++j) {
+            float aj = 0.0f;
+            for (int k = 16 * j; k < 16 * j + 16; ++k)
+                if (fabsf(v[k]) > aj) aj = fabsf(v[k]);
+            uint8_t f = 0;
+            if (amax > 0.0f) {
+                float ratio = aj / amax;
+                f = oracle_e4m3_encode(ratio * 448.0f);
+            }
+            f8[i * (int64_t)(K / 16) + j] = f;
+            const float S = sr * oracle_e4m3_decode(f);
+            for (int k = 16 * j; k < 16 * j + 16; ++k) {
+                float c = 0.0f;
+                if (S != 0.0f) {
+                    c = rintf(v[k] / S);
+                    if (c > (float)qmax) c = (float)qmax;
+                    if (c < -(float)qmax) c = -(float)qmax;
+                }
+                q[i * (int64_t)K + k] = (int8_t)c;
+            }
+        }
+    }
+}
+
+/* Weight converter: rows of w [N, K] bf16 rotated along K (group g), then quantised per group of 16.
+ * bits = 6: q_out [N, 3K/4] bytes; bits = 4: [N, K/2] nibble-packed.  codes_out (optional) [N, K] int8. */
+int oracle_quantize_g16(const uint16_t* w, int N, int K, int g, int bits, uint8_t* q_out, uint8_t* f8_out,
+                        float* s_out, int8_t* codes_out) {
+    if ((bits != 6 && bits != 4) || K % 16) return -1;
+    float* r = (float*)malloc(sizeof(float) * (size_t)N * (size_t)K);
+    int8_t* q = (int8_t*)malloc((size_t)N * (size_t)K);
+    int st = -2;
+    if (r && q) {
+        st = oracle_rotate_rows_bf16(w, N, K, g, r);
+        if (st == 0) {
+            oracle_quantize_g16_rows(r, N, K, bits == 6 ? 31 : 7, q, f8_out, s_out);
+            if (bits == 6)
+                oracle_pack_int6(q, N, K, q_out);
+            else
+                oracle_pack_int4(q, N, K, q_out);
+            if (codes_out) memcpy(codes_out, q, (size_t)N * (size_t)K);
+        }
+    }
+    free(r);
+    free(q);
+    return st;
+}
+
+/* The W6A8 / W4A8 linear on given token codes qx [M, K], sx [M] and weight codes q [N, K] (int8 holding the
+ * 6- or 4-bit values), f8 [N, K/16], s_row [N]:
+ *   A[m, n] = sum_k qx[m, k] * (q[n, k] * f(n, k/16)), exact (each term is an integer times a multiple of
+ *   2^-9 below 2^21, so |A| < 2^34 in steps of 2^-9 fits the 53-bit fp64 significand), rounded once to fp32;
+ *   y = bf16(((float)A * sx[m]) * s_row[n]) (+ bias[n] in fp32 before the rounding).
+ * acc_out (optional) gets A in fp64 and abs_out (optional) the sum of |terms|, for error bounds. */
+void oracle_gemm_g16(const int8_t* qx, const float* sx, int M, int K, const int8_t* q, const uint8_t* f8,
+                     const float* s_row, int N, const uint16_t* bias, uint16_t* y, double* acc_out,
+                     double* abs_out) {
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double a = 0.0, aa = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double wk = (double)q[(int64_t)n * K + k] * (double)oracle_e4m3_decode(f8[(int64_t)n * (K / 16) + k / 16]);
+                double term = (double)qx[(int64_t)m * K + k] * wk;
+                a += term;
+                aa += fabs(term);
+            }
+            float v = (float)a;
+            v = v * sx[m];
+            v = v * s_row[n];
+            if (bias) v = v + bf16_to_f32(bias[n]);
+            y[(int64_t)m * N + n] = f32_to_bf16(v);
+            if (acc_out) acc_out[(int64_t)m * N + n] = a;
+            if (abs_out) abs_out[(int64_t)m * N + n] = aa;
+        }
 }
 
 /* ------------------------------------------------------------------------------------------------- */

@@ -483,3 +483,96 @@ def test_lora_requant_rounding_is_unbiased_and_seeded(orc):
     q3, _ = orc.requantize_lora(q, s, g, lb, la, 1.0, seed=21)
     q4, _ = orc.requantize_lora(q, s, g, lb, la, 1.0, seed=22)
     assert np.array_equal(q3, q2) and not np.array_equal(q4, q2)
+
+
+# ----------------------------------------------------------------------------------------------------------
+# W6A8 / W4A8: FP8 (E4M3) scale per group of 16 (NitroFusion2 page, "How they were made")
+# ----------------------------------------------------------------------------------------------------------
+
+def test_e4m3_decode_fixed_points():
+    import oracle
+    got = oracle.e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x39, 0x7e, 0x80, 0xb8], np.uint8))
+    want = np.array([0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 448.0, -0.0, -1.0], np.float32)
+    assert np.array_equal(got, want) and np.signbit(got[7])
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7f, 0xff], np.uint8))).all()
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """Nearest-even rounding onto the E4M3 grid, against torch's float8_e4m3fn conversion (values up to 448,
+    where the two agree by definition; above it the oracle saturates)."""
+    import oracle
+    import torch
+    grid = oracle.e4m3_decode(np.arange(0x7f, dtype=np.uint8))  # every non-negative finite value
+    mids = (grid[:-1] + grid[1:]) / 2  # exact ties
+    rng = np.random.default_rng(7)
+    rnd = np.concatenate([rng.uniform(0, 448, 20000), np.exp2(rng.uniform(-12, 8.8, 20000))]).astype(np.float32)
+    x = np.concatenate([grid, mids.astype(np.float32), np.nextafter(mids, 0).astype(np.float32),
+                        np.nextafter(mids, 1000).astype(np.float32), rnd[rnd <= 448]])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x), ref)
+    assert np.array_equal(oracle.e4m3_encode(grid), np.arange(0x7f, dtype=np.uint8))
+    assert oracle.e4m3_encode(np.array([500.0, 1e9], np.float32)).tolist() == [0x7e, 0x7e]
+
+
+def test_int6_packing_layout():
+    import oracle
+    q = np.array([[1, -1, 31, -32, 0, 5, -7, 30]], np.int8)
+    p = oracle.pack_int6(q)
+    w0 = 1 | (63 << 6) | (31 << 12) | (32 << 18)
+    w1 = 0 | (5 << 6) | ((64 - 7) << 12) | (30 << 18)
+    assert p.tolist() == [[w0 & 255, (w0 >> 8) & 255, w0 >> 16, w1 & 255, (w1 >> 8) & 255, w1 >> 16]]
+    rng = np.random.default_rng(3)
+    r = rng.integers(-32, 32, (5, 64)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_int6(oracle.pack_int6(r), 64), r)
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_quantize_g16_properties(bits):
+    """Codes within +-qmax and, where not clamped, within half a group step of the rotated value (a group
+    scale rounded down onto the E4M3 grid can push its largest values past qmax: those clamp, off by at most
+    the scale's rounding, 2^-4 relative); the largest group's FP8 scale is 448; an all-zero row quantises to
+    zero; finer codes approximate better."""
+    import oracle
+    qmax = 31 if bits == 6 else 7
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    w[2] = 0.0
+    w[4, :16] *= 1e-4  # one group far below the row's largest
+    wb = oracle.bf16_round(w)
+    q, f8, s, codes = oracle.quantize_g16(wb, 256, bits)
+    assert np.array_equal(oracle.unpack_g16(q, 512, bits), codes)
+    r = oracle.rotate_rows_bf16(wb, 256).astype(np.float64)
+    S = s[:, None].astype(np.float64) * np.repeat(oracle.e4m3_decode(f8), 16, axis=1)
+    assert np.abs(codes).max() <= qmax
+    nz = S > 0
+    inner = nz & (np.abs(codes) < qmax)
+    clamped = nz & (np.abs(codes) == qmax)
+    assert (np.abs(r - codes * S)[inner] <= S[inner] / 2 * (1 + 1e-6)).all()
+    assert (np.abs(r)[clamped] >= (qmax - 0.5) * S[clamped] * (1 - 1e-6)).all()
+    assert (np.abs(r - codes * S)[clamped] <= 2.0 ** -4 * np.abs(r)[clamped] + S[clamped] / 2).all()
+    assert (codes[~nz] == 0).all()
+    assert not codes[2].any() and s[2] == 0 and not f8[2].any()
+    for i in (0, 1, 3, 4, 5):
+        assert f8[i].max() == 0x7e and np.isclose(s[i], np.abs(r[i]).max() / (qmax * 448), rtol=1e-6)
+    err = np.linalg.norm(r - codes * S) / np.linalg.norm(r)
+    assert err < (0.03 if bits == 6 else 0.15)
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_linear_g16_exact_sum_and_rotation_invariance(bits):
+    """The oracle's A is the exact dot product of the token codes with the decoded weights (checked by a
+    float64 matmul, exact here), and y approximates x W^T (rotation invariance) within quantisation error."""
+    import oracle
+    rng = np.random.default_rng(5)
+    M, K, N = 7, 512, 9
+    x = oracle.bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    w = oracle.bf16_round((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    q, f8, s, codes = oracle.quantize_g16(w, 256, bits)
+    y, qx, sx, acc, aabs = oracle.linear_g16(x, 256, codes, f8, s)
+    wdec = codes.astype(np.float64) * np.repeat(oracle.e4m3_decode(f8), 16, axis=1)
+    assert np.array_equal(acc, qx.astype(np.float64) @ wdec.T)
+    assert np.array_equal(aabs, np.abs(qx.astype(np.float64)) @ np.abs(wdec).T)
+    ref = oracle.bf16_to_f32(x).astype(np.float64) @ oracle.bf16_to_f32(w).astype(np.float64).T
+    got = oracle.bf16_to_f32(y).astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < (0.05 if bits == 6 else 0.2)
