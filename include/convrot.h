@@ -206,6 +206,46 @@ convrot_status convrot_gemm_w8a8_bf16(const int8_t* qx, const float* sx, int M, 
                                       const float* sw, int N, const uint16_t* bias, uint16_t* y,
                                       hipStream_t stream);
 
+/* ---- W6A8 / W4A8 with an FP8 scale per group of 16 -----------------------------------------------------
+ * "NitroFusion2 for ComfyUI: int8, W6A8, W4A8", "How they were made": 6- or 4-bit weights in the rotated
+ * basis with an FP8 scale per group of 16, 8-bit activations.  The page fixes only the bit widths, the
+ * group size and the scale type; the library reads it as follows.
+ *  - Rotation: the block Hadamard above (group 64 or 256 along K), fp32, as for the int8 weights.
+ *  - Codes: symmetric integers, qmax = 31 (bits = 6) or 7 (bits = 4), nearest rounding, ties to even.
+ *  - Scales: FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite 448),
+ *    one per 16 consecutive k, relative to one fp32 scale per row (E4M3 cannot hold the absolute group
+ *    scales of typical weights):  s_row = amax / (qmax * 448);  f_j = E4M3((amax_j / amax) * 448), nearest
+ *    E4M3 value with ties to the even mantissa;  code = clamp(rint(r / (s_row * f_j)), +-qmax), 0 where
+ *    s_row * f_j = 0.  Each step is one IEEE fp32 operation in the order written.
+ *  - Layouts, row-major: q [N, K/2] (4-bit: two's-complement nibbles, even k in bits 0-3) or [N, 3K/4]
+ *    (6-bit: codes 4j..4j+3 of a row in bytes 3j..3j+2, code 4j+i in bits 6i..6i+5 of the little-endian
+ *    24-bit word); f8 [N, K/16] E4M3 bytes; s_row [N] fp32.
+ *  - Linear: tokens rotated and quantised to int8 per token as for W8A8; then
+ *    y[m, n] = bf16( ((float)A[m, n] * sx[m]) * s_row[n] ) (+ bias[n] in fp32), A = sum_k qx[m, k] *
+ *    (code[n, k] * f(n, k / 16)).  The kernel accumulates A in fp32 (every product exact), so y differs from
+ *    the exactly summed A by the fp32 accumulation error only. */
+
+/* Bytes of the packed codes of an [N, K] weight: N * K * bits / 8. */
+size_t convrot_weight_g16_bytes(int N, int K, int bits);
+
+/* Converter: w (device) [N, K] bf16 -> q_out (device, convrot_weight_g16_bytes bytes), f8_out (device)
+ * [N, K/16] E4M3, s_out (device) [N] fp32.  Requires N >= 1, group in {64, 256}, K % group == 0,
+ * K <= 8192, bits in {4, 6} (CONVROT_ERR_BITS otherwise).  Non-finite weights are outside the contract. */
+convrot_status convrot_quantize_weights_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q_out,
+                                            uint8_t* f8_out, float* s_out, hipStream_t stream);
+
+/* GEMM stage on quantised tokens qx (device) [M, K] int8 and sx (device) [M] (convrot_rotq_rows with the
+ * weights' group): y (device) [M, N] bf16 as above; bias (device) [N] bf16 or NULL.  Requires M, N >= 1,
+ * 32 <= K <= 8192, K % 32 == 0, bits in {4, 6}. */
+convrot_status convrot_gemm_g16_bf16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw,
+                                     const uint8_t* f8, const float* s_row, int N, int bits, const uint16_t* bias,
+                                     uint16_t* y, hipStream_t stream);
+
+/* The whole linear: x (device) [M, K] bf16; workspace as convrot_linear_workspace_bytes(M, K). */
+convrot_status convrot_linear_g16(const uint16_t* x, int M, int K, const uint8_t* qw, const uint8_t* f8,
+                                  const float* s_row, int N, int group, int bits, const uint16_t* bias, uint16_t* y,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of workspace moe_route_expert_choice needs. */
 size_t moe_route_workspace_bytes(int T, int E);
 

@@ -18,10 +18,33 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 21
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
+
+
+def test_g16_validation(L):
+    assert L.convrot_weight_g16_bytes(3, 512, 6) == 3 * 384 and L.convrot_weight_g16_bytes(3, 512, 4) == 3 * 256
+    assert L.convrot_weight_g16_bytes(3, 512, 5) == 0
+    f = L.convrot_quantize_weights_g16
+    assert f(None, 4, 512, 256, 6, P, P, P, None) == NULL
+    assert f(P, 4, 512, 256, 5, P, P, P, None) == BITS
+    assert f(P, 4, 500, 256, 6, P, P, P, None) == GROUP
+    assert f(P, 4, 128, 256, 6, P, P, P, None) == GROUP
+    assert f(P, 0, 512, 256, 6, P, P, P, None) == SHAPE
+    assert f(P, 4, 16384, 256, 6, P, P, P, None) == SHAPE
+    assert f(P + 2, 4, 512, 256, 6, P, P, P, None) == ALIGN
+    g = L.convrot_gemm_g16_bf16
+    assert g(P, P, 8, 512, P, P, P, 16, 8, None, P, None) == BITS
+    assert g(P, P, 8, 48, P, P, P, 16, 4, None, P, None) == SHAPE
+    assert g(P, P, 0, 512, P, P, P, 16, 4, None, P, None) == SHAPE
+    assert g(P, P, 8, 512, P, P, P, 16, 4, P + 4, P, None) == ALIGN
+    lin = L.convrot_linear_g16
+    need = L.convrot_linear_workspace_bytes(8, 512)
+    assert lin(P, 8, 512, P, P, P, 16, 256, 6, None, P, P, need - 1, None) == WS
+    assert lin(P, 8, 500, P, P, P, 16, 256, 6, None, P, P, need, None) == GROUP
+    assert lin(P, 8, 512, None, P, P, 16, 256, 6, None, P, P, need, None) == NULL
 
 
 def test_probe_validation(L):

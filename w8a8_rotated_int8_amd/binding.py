@@ -59,6 +59,10 @@ _SIGS = {
     "moe_down_proj": (_i, [_p, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p]),
     "moe_combine_workspace_bytes": (_sz, [_i, _i]),
     "moe_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "convrot_weight_g16_bytes": (_sz, [_i, _i, _i]),
+    "convrot_quantize_weights_g16": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "convrot_gemm_g16_bf16": (_i, [_p, _p, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p]),
+    "convrot_linear_g16": (_i, [_p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p, _sz, _p]),
     "convrot_probe_out_words": (_sz, []),
     "convrot_probe_mfma_i8": (_i, [_p, _sz, _i, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
     "convrot_probe_hbm_read": (_i, [_p, _sz, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
@@ -287,6 +291,40 @@ def convrot_gemm_w8a8_bf16(qx, sx, qw, sw, bias=None, y=None, stream=None):
         y = _empty((M, N), torch.bfloat16, qx)
     _check("convrot_gemm_w8a8_bf16", lib().convrot_gemm_w8a8_bf16(
         _ptr(qx), _ptr(sx), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y), _stream(stream)))
+    return y
+
+
+def convrot_quantize_weights_g16(w, group: int, bits: int, stream=None):
+    """w: bf16 [N, K].  Returns (packed codes u8 [N, K*bits/8], E4M3 group scales u8 [N, K/16], row scales
+    fp32 [N]) in the W6A8 / W4A8 format."""
+    N, K = w.shape
+    q = _empty((N, K * bits // 8), torch.uint8, w)
+    f8 = _empty((N, K // 16), torch.uint8, w)
+    s = _empty((N,), torch.float32, w)
+    _check("convrot_quantize_weights_g16", lib().convrot_quantize_weights_g16(
+        _ptr(w), N, K, group, bits, _ptr(q), _ptr(f8), _ptr(s), _stream(stream)))
+    return q, f8, s
+
+
+def convrot_gemm_g16_bf16(qx, sx, q, f8, s_row, bits: int, bias=None, y=None, stream=None):
+    M, K = qx.shape
+    N = s_row.shape[0]
+    if y is None:
+        y = _empty((M, N), torch.bfloat16, qx)
+    _check("convrot_gemm_g16_bf16", lib().convrot_gemm_g16_bf16(
+        _ptr(qx), _ptr(sx), M, K, _ptr(q), _ptr(f8), _ptr(s_row), N, bits, _ptr(bias), _ptr(y), _stream(stream)))
+    return y
+
+
+def convrot_linear_g16(x, q, f8, s_row, group: int, bits: int, bias=None, y=None, ws=None, stream=None):
+    M, K = x.shape
+    N = s_row.shape[0]
+    if y is None:
+        y = _empty((M, N), torch.bfloat16, x)
+    ws = _workspace(lib().convrot_linear_workspace_bytes(M, K), x, ws)
+    _check("convrot_linear_g16", lib().convrot_linear_g16(
+        _ptr(x), M, K, _ptr(q), _ptr(f8), _ptr(s_row), N, group, bits, _ptr(bias), _ptr(y), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return y
 
 

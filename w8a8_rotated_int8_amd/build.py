@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libconvrot_amd.so")
-SOURCES = ["rotq.hip", "route.hip", "gemm.hip", "combine.hip", "peaks.hip", "convrot_api.cpp"]
+SOURCES = ["rotq.hip", "route.hip", "gemm.hip", "combine.hip", "g16.hip", "peaks.hip", "convrot_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

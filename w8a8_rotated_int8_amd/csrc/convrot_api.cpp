@@ -255,6 +255,55 @@ convrot_status convrot_gemm_w8a8_bf16(const int8_t* qx, const float* sx, int M, 
     return hip_status(crk::launch_grouped_gemm(p, stream));
 }
 
+size_t convrot_weight_g16_bytes(int N, int K, int bits) {
+    if (N < 1 || K < 1 || (bits != 4 && bits != 6)) return 0;
+    return (size_t)N * (size_t)K * (size_t)bits / 8;
+}
+
+convrot_status convrot_quantize_weights_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q_out,
+                                            uint8_t* f8_out, float* s_out, hipStream_t stream) {
+    if (!w || !q_out || !f8_out || !s_out) return CONVROT_ERR_NULL;
+    if (bits != 4 && bits != 6) return CONVROT_ERR_BITS;
+    if (!group_ok(group) || K < group || K % group) return CONVROT_ERR_GROUP;
+    if (N < 1 || K > kMaxRowLen) return CONVROT_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(q_out) || !aligned16(f8_out) || !aligned16(s_out)) return CONVROT_ERR_ALIGN;
+    CRK_TRY(crk::launch_quantize_g16(w, N, K, group, bits, q_out, f8_out, s_out, stream));
+    return CONVROT_OK;
+}
+
+convrot_status convrot_gemm_g16_bf16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw,
+                                     const uint8_t* f8, const float* s_row, int N, int bits, const uint16_t* bias,
+                                     uint16_t* y, hipStream_t stream) {
+    if (!qx || !sx || !qw || !f8 || !s_row || !y) return CONVROT_ERR_NULL;
+    if (bits != 4 && bits != 6) return CONVROT_ERR_BITS;
+    if (M < 1 || N < 1 || K < 32 || K > kMaxRowLen || K % 32 || (M + 127) / 128 > 65535) return CONVROT_ERR_SHAPE;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(f8) || !aligned16(s_row) ||
+        !aligned16(y) || (bias && !aligned16(bias)))
+        return CONVROT_ERR_ALIGN;
+    CRK_TRY(crk::launch_gemm_g16(qx, sx, M, K, qw, f8, s_row, N, bits, bias, y, stream));
+    return CONVROT_OK;
+}
+
+convrot_status convrot_linear_g16(const uint16_t* x, int M, int K, const uint8_t* qw, const uint8_t* f8,
+                                  const float* s_row, int N, int group, int bits, const uint16_t* bias, uint16_t* y,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !qw || !f8 || !s_row || !y) return CONVROT_ERR_NULL;
+    if (bits != 4 && bits != 6) return CONVROT_ERR_BITS;
+    if (M < 1 || N < 1 || K < 1 || K > kMaxRowLen || (M + 127) / 128 > 65535) return CONVROT_ERR_SHAPE;
+    if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(f8) || !aligned16(s_row) || !aligned16(y) ||
+        (bias && !aligned16(bias)))
+        return CONVROT_ERR_ALIGN;
+    if (!ws || ws_bytes < convrot_linear_workspace_bytes(M, K)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+    Carver cv(ws);
+    int8_t* qx = cv.take<int8_t>((size_t)M * K);
+    float* sx = cv.take<float>((size_t)M);
+    CRK_TRY(crk::launch_rotq_act(x, M, K, group, qx, sx, nullptr, stream));
+    CRK_TRY(crk::launch_gemm_g16(qx, sx, M, K, qw, f8, s_row, N, bits, bias, y, stream));
+    return CONVROT_OK;
+}
+
 size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights* w) {
     if (!w || T < 1 || C < 1 || w->E < 1 || w->d < 1 || w->I < 1) return 0;
     return plan_moe(nullptr, T, C, *w, nullptr);

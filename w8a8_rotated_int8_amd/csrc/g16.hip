@@ -1,0 +1,307 @@
+// W6A8 / W4A8 linears: 6- or 4-bit weight codes in the rotated basis with an FP8 scale per group of 16
+// ("NitroFusion2 for ComfyUI: int8, W6A8, W4A8", "How they were made"), 8-bit activations.
+//
+// Format (the library's reading of the page, as in include/convrot.h):
+//   - rotation: the same block Hadamard as the int8 format, in fp32;
+//   - codes: symmetric integers, qmax = 31 (6 bits) or 7 (4 bits), nearest rounding, ties to even;
+//   - FP8 = E4M3 (bias 7, 3 mantissa bits, subnormals, largest 448), one per 16 consecutive k, relative to one
+//     fp32 scale per row: s_row = amax / (qmax * 448), f = E4M3((amax_group / amax) * 448), the group's scale
+//     s_row * f, code = clamp(rint(r / (s_row * f)), +-qmax);
+//   - packing: 4-bit as two's-complement nibbles, even k low; 6-bit codes 4j..4j+3 in the little-endian
+//     24-bit word j (code 4j+i in bits 6i..6i+5).
+//
+// The GEMM multiplies in fp16 on the matrix cores: an int8 activation code and a decoded weight code * f are
+// both exact in fp16 (at most 9 significant bits, within its range), so every product is exact in the fp32
+// accumulator; y = bf16((acc * s_x) * s_row) (+ bias).
+#include <cstddef>
+#include <cstdint>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace crk {
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---- E4M3 -------------------------------------------------------------------------------------------------
+// Non-negative fp32 -> E4M3 byte, nearest value with ties to the even mantissa; 448 and above give 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    if (!(x > 0.0f)) return 0u;
+    if (x >= 448.0f) return 0x7eu;
+    int E = (int)(__float_as_uint(x) >> 23) - 127;  // x in [2^E, 2^(E+1)) (fp32 subnormals round to 0 below)
+    if (E < -6) E = -6;                             // the subnormal spacing 2^-9 continues below 2^-6
+    int n = (int)rintf(ldexpf(x, 3 - E));           // x in units of the spacing 2^(E-3)
+    if (E == -6 && n < 8) return (uint32_t)n;
+    if (n == 16) {
+        E += 1;
+        n = 8;
+    }
+    return (uint32_t)(((E + 7) << 3) | (n - 8));
+}
+// E4M3 byte (no NaN code) -> value.
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+    const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+    const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+    return (b & 0x80u) ? -v : v;
+}
+
+// ---- converter: one workgroup per row ---------------------------------------------------------------------
+// The row is rotated in LDS by the fast transform, stage by stage (h = 1, 2, ..., g/2, pairs (i, i + h) with
+// bit h of i's offset clear becoming (a + b, a - b)), then scaled by 2^-(log2 g)/2; then each group of 16 is
+// quantised by one thread.
+constexpr int kConvThreads = 256;
+
+template <int BITS>
+__global__ __launch_bounds__(kConvThreads) void quantize_g16_kernel(const uint16_t* __restrict__ w, int K, int g,
+                                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ f8,
+                                                                    float* __restrict__ s_row) {
+    constexpr int kQmax = BITS == 6 ? 31 : 7;
+    extern __shared__ float row[];
+    __shared__ float red[kConvThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t n = blockIdx.x;
+    for (int k = tid; k < K; k += kConvThreads) row[k] = bf16_to_float(w[n * K + k]);
+    __syncthreads();
+    const int half = g / 2;
+    for (int h = 1; h < g; h *= 2) {
+        for (int p = tid; p < K / 2; p += kConvThreads) {
+            const int blk = p / half, j = p % half;
+            const int i0 = blk * g + (j / h) * 2 * h + (j % h);
+            const float a = row[i0], b = row[i0 + h];
+            row[i0] = a + b;
+            row[i0 + h] = a - b;
+        }
+        __syncthreads();
+    }
+    const float norm = g == 256 ? 0.0625f : 0.125f;  // 2^-(log2 g)/2, exact
+    float amax = 0.0f;
+    for (int k = tid; k < K; k += kConvThreads) {
+        const float v = row[k] * norm;
+        row[k] = v;
+        amax = fmaxf(amax, fabsf(v));
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sr = amax / (float)(kQmax * 448);
+    if (tid == 0) s_row[n] = sr;
+    const int groups = K / 16;
+    for (int j = tid; j < groups; j += kConvThreads) {
+        const float* v = row + 16 * j;
+        float aj = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) aj = fmaxf(aj, fabsf(v[i]));
+        uint32_t f = 0u;
+        if (amax > 0.0f) {
+            const float ratio = aj / amax;
+            f = e4m3_encode(ratio * 448.0f);
+        }
+        f8[n * groups + j] = (uint8_t)f;
+        const float S = sr * e4m3_decode(f);
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float t = 0.0f;
+            if (S != 0.0f) t = fminf(fmaxf(rintf(v[i] / S), -(float)kQmax), (float)kQmax);
+            c[i] = (int)t;
+        }
+        if constexpr (BITS == 4) {
+            uint8_t* o = q + n * (K / 2) + 8 * j;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) o[b] = (uint8_t)((c[2 * b] & 15) | ((c[2 * b + 1] & 15) << 4));
+        } else {
+            uint8_t* o = q + n * (K / 4 * 3) + 12 * j;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t wd = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wd |= ((uint32_t)c[4 * u + i] & 63u) << (6 * i);
+                o[3 * u] = (uint8_t)wd;
+                o[3 * u + 1] = (uint8_t)(wd >> 8);
+                o[3 * u + 2] = (uint8_t)(wd >> 16);
+            }
+        }
+    }
+}
+
+// ---- GEMM + dequant ---------------------------------------------------------------------------------------
+// Workgroup tile 128 tokens x 128 weight rows, 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), K in steps
+// of 32 (two groups).  Each step is staged in LDS already decoded to fp16 (tokens: code; weights: code * f),
+// double-buffered: the next step's global loads are in flight while the current one is multiplied.
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kGemmThreads = 256;
+constexpr int kRowHalves = kBK + 8;  // LDS row pitch (80 bytes) spreads the fragment reads over the banks
+
+template <int BITS>
+struct StageRegs {
+    uint4 a;                       // 16 token codes
+    uint32_t b[BITS == 6 ? 3 : 2];  // 16 packed weight codes
+    uint32_t f;                     // their E4M3 scale
+};
+
+template <int BITS>
+__device__ __forceinline__ void stage_load(StageRegs<BITS>& r, const int8_t* __restrict__ qx, int M, int K,
+                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ f8, int N,
+                                           int m0, int n0, int k0) {
+    const int t = threadIdx.x, row = t >> 1, hk = t & 1;
+    const int m = min(m0 + row, M - 1), n = min(n0 + row, N - 1);  // rows past the end compute unused outputs
+    r.a = *reinterpret_cast<const uint4*>(qx + (int64_t)m * K + k0 + 16 * hk);
+    const int grp = k0 / 16 + hk;
+    if constexpr (BITS == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(qw + (int64_t)n * (K / 2) + 8 * grp);
+        r.b[0] = v.x;
+        r.b[1] = v.y;
+    } else {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(qw + (int64_t)n * (K / 4 * 3) + 12 * grp);
+        r.b[0] = p[0];
+        r.b[1] = p[1];
+        r.b[2] = p[2];
+    }
+    r.f = f8[(int64_t)n * (K / 16) + grp];
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* As, _Float16* Bs) {
+    const int t = threadIdx.x, row = t >> 1, hk = t & 1;
+    _Float16 ha[16], hb[16];
+    const uint32_t aw[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ha[i] = (_Float16)(int)(int8_t)(aw[i >> 2] >> (8 * (i & 3)));
+    const float f = e4m3_decode(r.f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int c;
+        if constexpr (BITS == 4) {
+            c = (int)((r.b[i >> 3] >> (4 * (i & 7))) & 15u);
+            c = c >= 8 ? c - 16 : c;
+        } else {
+            // code i of the group: word i / 4 of 24 bits starts at bit 24 * (i / 4) of the 96-bit run
+            const int bit = 24 * (i >> 2) + 6 * (i & 3);
+            const uint32_t lo = r.b[bit >> 5] >> (bit & 31);
+            const uint32_t hi = (bit & 31) > 26 ? (r.b[(bit >> 5) + 1] << (32 - (bit & 31))) : 0u;
+            c = (int)((lo | hi) & 63u);
+            c = c >= 32 ? c - 64 : c;
+        }
+        hb[i] = (_Float16)((float)c * f);  // exact: at most 9 significant bits
+    }
+    _Float16* ao = As + row * kRowHalves + 16 * hk;
+    _Float16* bo = Bs + row * kRowHalves + 16 * hk;
+    *reinterpret_cast<v8h*>(ao) = v8h{ha[0], ha[1], ha[2], ha[3], ha[4], ha[5], ha[6], ha[7]};
+    *reinterpret_cast<v8h*>(ao + 8) = v8h{ha[8], ha[9], ha[10], ha[11], ha[12], ha[13], ha[14], ha[15]};
+    *reinterpret_cast<v8h*>(bo) = v8h{hb[0], hb[1], hb[2], hb[3], hb[4], hb[5], hb[6], hb[7]};
+    *reinterpret_cast<v8h*>(bo + 8) = v8h{hb[8], hb[9], hb[10], hb[11], hb[12], hb[13], hb[14], hb[15]};
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __restrict__ qx,
+                                                                const float* __restrict__ sx, int M, int K,
+                                                                const uint8_t* __restrict__ qw,
+                                                                const uint8_t* __restrict__ f8,
+                                                                const float* __restrict__ s_row, int N,
+                                                                const uint16_t* __restrict__ bias,
+                                                                uint16_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kRowHalves];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kBN * kRowHalves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+    const int nk = K / kBK;
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    StageRegs<BITS> regs;
+    stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, 0);
+    stage_store<BITS>(regs, As[0], Bs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, (kt + 1) * kBK);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            // fragment: row lane % 32 of a 32-row block, halves 16 s + 8 (lane / 32) .. + 8
+            const int col = 16 * s + 8 * (lane >> 5);
+            v8h af[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const v8h*>(As[buf] + (wm * 64 + 32 * i + (lane & 31)) * kRowHalves + col);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bf[j] = *reinterpret_cast<const v8h*>(Bs[buf] + (wn * 64 + 32 * j + (lane & 31)) * kRowHalves + col);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) stage_store<BITS>(regs, As[buf ^ 1], Bs[buf ^ 1]);
+        __syncthreads();
+    }
+
+    // The weights are the MFMA's first operand: lane l holds token l % 32 of each 32 x 32 block and, in
+    // register 4 q + i, weight row 8 q + 4 (l / 32) + i.
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+        if (m >= M) continue;
+        const float sm = sx[m];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int nb = n0 + wn * 64 + 32 * j + 8 * qd + 4 * (lane >> 5);
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = min(nb + e, N - 1);
+                    float v = acc[i][j][4 * qd + e];
+                    v = v * sm;
+                    v = v * s_row[n];
+                    if (bias) v = v + bf16_to_float(bias[n]);
+                    h[e] = float_to_bf16(v);
+                }
+                uint16_t* out = y + (int64_t)m * N + nb;
+                if (vec && nb + 3 < N) {
+                    *reinterpret_cast<uint2*>(out) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (nb + e < N) out[e] = (uint16_t)h[e];
+                }
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q, uint8_t* f8,
+                               float* s_row, hipStream_t st) {
+    if (N == 0) return hipSuccess;
+    const size_t lds = sizeof(float) * (size_t)K;
+    if (bits == 6)
+        quantize_g16_kernel<6><<<dim3((unsigned)N), dim3(kConvThreads), lds, st>>>(w, K, group, q, f8, s_row);
+    else
+        quantize_g16_kernel<4><<<dim3((unsigned)N), dim3(kConvThreads), lds, st>>>(w, K, group, q, f8, s_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_g16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw, const uint8_t* f8,
+                           const float* s_row, int N, int bits, const uint16_t* bias, uint16_t* y, hipStream_t st) {
+    const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(kGemmThreads);
+    if (bits == 6)
+        gemm_g16_kernel<6><<<grid, block, 0, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
+    else
+        gemm_g16_kernel<4><<<grid, block, 0, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
+    return hipGetLastError();
+}
+
+}  // namespace crk

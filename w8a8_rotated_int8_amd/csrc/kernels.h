@@ -16,6 +16,11 @@ hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, in
 hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, int N, int K, int group,
                                   const uint16_t* lb, const uint16_t* la, int rank, float alpha, uint64_t seed,
                                   bool tiled, int8_t* qout, float* sout, hipStream_t st);
+// W6A8 / W4A8 with E4M3 group-16 scales: converter (row-major packing) and GEMM + dequant
+hipError_t launch_quantize_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q, uint8_t* f8,
+                               float* s_row, hipStream_t st);
+hipError_t launch_gemm_g16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw, const uint8_t* f8,
+                           const float* s_row, int N, int bits, const uint16_t* bias, uint16_t* y, hipStream_t st);
 hipError_t launch_rotq_weights(const uint16_t* w, int E, int N, int K, int group, int bits, bool tiled, void* q,
                                float* s, hipStream_t st);
 hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int bits, int8_t* q, float* s,
