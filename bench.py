@@ -6,7 +6,8 @@ probability-weighted combine.  Weights are converted once before timing (offline
 resident in HBM when the timed region starts.
 
 --workload dense times one dense W8A8 ConvRot linear over the same 8192 tokens instead (rotate+quantise of the
-tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection).  --workload lora times the load-time
+tokens + INT8 GEMM with dequant to bf16; --dense-shape picks the projection); --workload g16 the same linear
+with 4- or 6-bit weights and an E4M3 scale per group of 16 (--g16-bits).  --workload lora times the load-time
 LoRA patch of the layer's quantised gate/up weights (64 x [3072, 2048], rank 32), re-quantised with random
 rounding into the layout the GEMM streams.
 
@@ -212,6 +213,103 @@ def run_dense(args):
     print(json.dumps(line), flush=True)
 
 
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, TFLOP/s
+
+
+def run_g16(args):
+    """The W6A8 / W4A8 dense linear (E4M3 scale per group of 16): rotate+quantise of the tokens + the GEMM
+    whose matrix cores multiply exact fp16 products."""
+    import torch
+    from w8a8_rotated_int8_amd import binding as cr
+    from w8a8_rotated_int8_amd import synth
+
+    dev = torch.device("cuda:0")
+    name, bits = args.dense_shape, args.g16_bits
+    M, K, N, g = synth.DENSE_SHAPES[name]
+    with_bias = name == "out"
+    print(f"bench: g16 {name} M={M} K={K} N={N} g={g} bits={bits} bias={with_bias}", file=sys.stderr, flush=True)
+    x, w, b = synth.dense_linear_inputs(M, K, N, with_bias)
+
+    def bf16_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xd, bd = bf16_dev(x), (None if b is None else bf16_dev(b))
+    q, f8, s = cr.convrot_quantize_weights_g16(bf16_dev(w), g, bits)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cr.convrot_linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cr.convrot_linear_g16(xd, q, f8, s, g, bits, bias=bd, y=y, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    qx, sx, _ = cr.convrot_rotq_rows(xd, g)
+    for _ in range(3):
+        cr.convrot_gemm_g16_bf16(qx, sx, q, f8, s, bits, bias=bd, y=y, stream=stream)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(args.kernel_iters):
+        cr.convrot_gemm_g16_bf16(qx, sx, q, f8, s, bits, bias=bd, y=y, stream=stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    k_us = k0.elapsed_time(k1) / args.kernel_iters * 1e3
+    ops = 2.0 * M * N * K
+    gemm_tflops = ops / (k_us * 1e-6) / 1e12
+    gemm_bytes = M * K + N * K * bits // 8 + N * K // 16 + M * 4 + N * 4 + (N * 2 if with_bias else 0) + M * N * 2
+    print(f"bench: {args.steps} steps, {ms * 1e3:.1f} us/step; GEMM {k_us:.1f} us/launch, {gemm_tflops:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": f"effective TOPS of one dense W{bits}A8 linear with E4M3 group-16 scales (rotate+quantise + GEMM)",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{bits}w-int8a (fp16 MFMA, fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x20, N(0,0.02) weights"
+                + (" and bias" if with_bias else "") + ")",
+        "config": {"workload": f"dense W{bits}A8 linear, E4M3 scale per 16 ({name}) M={M} K={K} N={N} group={g}"
+                               + (" with bias" if with_bias else ""), "M": M, "K": K, "N": N, "group": g,
+                   "bits": bits},
+        "tokens_per_s": round(M / (ms * 1e-3), 1),
+        "roofline": {"kernel": "group-16 GEMM + dequant (convrot_gemm_g16_bf16)", "bound": "mfma",
+                     "achieved": round(gemm_tflops, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP16_TFLOPS, 4), "traffic": None, "launch_us": round(k_us, 2),
+                     "hbm_frac": round(gemm_bytes / (k_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_experts > 0:
+        import oracle
+        rq, rf, rs, codes = oracle.quantize_g16(w, g, bits)
+        rows = 64
+        reps, dt = 0, 0.0
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        while reps == 0 or (dt < 10.0 and reps < 64):
+            t0 = time.perf_counter()
+            oracle.linear_g16(x[:rows], g, codes, rf, rs, b)
+            dt += time.perf_counter() - t0
+            reps += 1
+        line["cpu_baseline"] = {"value": 2.0 * rows * N * K * reps / dt / 1e12, "unit": "TOPS",
+                                "cores": cpu_cores(), "kind": "oracle",
+                                "sample": f"the linear on the first {rows} of the {M} token rows (all {N} outputs), "
+                                          f"run {reps} times in {dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 PEAK_VALU_OPS = 256 * 64 * 2.4e9 / 1e12  # fp32 VALU operations (no FMA) per second, T: 256 CUs x 64 lanes x 2.4 GHz
 
 
@@ -305,7 +403,9 @@ def main():
     ap.add_argument("--cpu-experts", type=int, default=64,
                     help="experts in the CPU-oracle sample of the MoE workload; 0 skips the CPU baseline (either workload)")
     ap.add_argument("--kernel-iters", type=int, default=50, help="timed launches of the dominant kernel")
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense", "lora"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense", "lora", "g16"])
+    ap.add_argument("--g16-bits", type=int, default=4, choices=[4, 6],
+                    help="weight bits of the group-16 workload (W4A8 or W6A8)")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the achievable-rate probes (int8 MFMA, HBM read) reported beside the roofline")
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
@@ -317,6 +417,8 @@ def main():
         return run_dense(args)
     if args.workload == "lora":
         return run_lora(args)
+    if args.workload == "g16":
+        return run_g16(args)
 
     import torch
     from w8a8_rotated_int8_amd import binding as cr
