@@ -163,36 +163,63 @@ __device__ __forceinline__ void stage_load(StageRegs<BITS>& r, const int8_t* __r
     r.f = f8[(int64_t)n * (K / 16) + grp];
 }
 
+// Decoding to fp16 with integer operations: for a code c in [-2^(b-1), 2^(b-1)), the half whose bits are
+// 0x6400 | (c + 2^(b-1)) is 1024 + c + 2^(b-1) exactly, so one packed fp16 subtraction of 1024 + 2^(b-1) gives
+// c, two codes per 32-bit register (and c * f is exact too).  The two codes of a register are k and k + 4 of an
+// 8-wide chunk, so a chunk is stored in the order k0, k4, k1, k5, k2, k6, k3, k7 -- for the tokens and the
+// weights alike, which leaves every dot product unchanged.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ h2 bits_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+
 template <int BITS>
 __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* As, _Float16* Bs) {
     const int t = threadIdx.x, row = t >> 1, hk = t & 1;
-    _Float16 ha[16], hb[16];
+    uint32_t a[8], b[8];
+    // tokens: bytes k and k + 4 of each 8-byte chunk into one register, sign bit flipped (x + 128 in 0..255)
     const uint32_t aw[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ha[i] = (_Float16)(int)(int8_t)(aw[i >> 2] >> (8 * (i & 3)));
-    const float f = e4m3_decode(r.f);
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        int c;
-        if constexpr (BITS == 4) {
-            c = (int)((r.b[i >> 3] >> (4 * (i & 7))) & 15u);
-            c = c >= 8 ? c - 16 : c;
-        } else {
-            // code i of the group: word i / 4 of 24 bits starts at bit 24 * (i / 4) of the 96-bit run
-            const int bit = 24 * (i >> 2) + 6 * (i & 3);
-            const uint32_t lo = r.b[bit >> 5] >> (bit & 31);
-            const uint32_t hi = (bit & 31) > 26 ? (r.b[(bit >> 5) + 1] << (32 - (bit & 31))) : 0u;
-            c = (int)((lo | hi) & 63u);
-            c = c >= 32 ? c - 64 : c;
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t x = __builtin_amdgcn_perm(aw[2 * c + 1], aw[2 * c], 0x0c040c00u + (uint32_t)(i | (i << 16)));
+            a[4 * c + i] = h2_bits(bits_h2(x ^ 0x64806480u) - h2{(_Float16)1152.0f, (_Float16)1152.0f});
         }
-        hb[i] = (_Float16)((float)c * f);  // exact: at most 9 significant bits
+    const _Float16 fh = (_Float16)e4m3_decode(r.f);  // every E4M3 value is an fp16 value
+    const h2 f2{fh, fh};
+    if constexpr (BITS == 4) {
+        // word c holds codes 8c..8c+7 as nibbles; (w >> 4i) & 0x000f000f puts codes i and i + 4 in the halves
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = (r.b[c] >> (4 * i)) & 0x000f000fu;
+                b[4 * c + i] =
+                    h2_bits((bits_h2(x ^ 0x64086408u) - h2{(_Float16)1032.0f, (_Float16)1032.0f}) * f2);
+            }
+    } else {
+        // code j at bit 6 j of the 96-bit run; alignbit takes a field that straddles two words
+        auto field = [&](int j) -> uint32_t {
+            const int p = 6 * j, w = p >> 5;
+            const uint32_t hi = w + 1 < 3 ? r.b[w + 1] : 0u;
+            return __builtin_amdgcn_alignbit(hi, r.b[w], (uint32_t)(p & 31)) & 63u;
+        };
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = field(8 * c + i) | (field(8 * c + i + 4) << 16);
+                b[4 * c + i] =
+                    h2_bits((bits_h2(x ^ 0x64206420u) - h2{(_Float16)1056.0f, (_Float16)1056.0f}) * f2);
+            }
     }
-    _Float16* ao = As + row * kRowHalves + 16 * hk;
-    _Float16* bo = Bs + row * kRowHalves + 16 * hk;
-    *reinterpret_cast<v8h*>(ao) = v8h{ha[0], ha[1], ha[2], ha[3], ha[4], ha[5], ha[6], ha[7]};
-    *reinterpret_cast<v8h*>(ao + 8) = v8h{ha[8], ha[9], ha[10], ha[11], ha[12], ha[13], ha[14], ha[15]};
-    *reinterpret_cast<v8h*>(bo) = v8h{hb[0], hb[1], hb[2], hb[3], hb[4], hb[5], hb[6], hb[7]};
-    *reinterpret_cast<v8h*>(bo + 8) = v8h{hb[8], hb[9], hb[10], hb[11], hb[12], hb[13], hb[14], hb[15]};
+    uint32_t* ao = reinterpret_cast<uint32_t*>(As + row * kRowHalves + 16 * hk);
+    uint32_t* bo = reinterpret_cast<uint32_t*>(Bs + row * kRowHalves + 16 * hk);
+    *reinterpret_cast<uint4*>(ao) = make_uint4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<uint4*>(ao + 4) = make_uint4(a[4], a[5], a[6], a[7]);
+    *reinterpret_cast<uint4*>(bo) = make_uint4(b[0], b[1], b[2], b[3]);
+    *reinterpret_cast<uint4*>(bo + 4) = make_uint4(b[4], b[5], b[6], b[7]);
 }
 
 template <int BITS>
