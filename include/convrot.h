@@ -236,7 +236,7 @@ convrot_status convrot_quantize_weights_g16(const uint16_t* w, int N, int K, int
 
 /* GEMM stage on quantised tokens qx (device) [M, K] int8 and sx (device) [M] (convrot_rotq_rows with the
  * weights' group): y (device) [M, N] bf16 as above; bias (device) [N] bf16 or NULL.  Requires M, N >= 1,
- * 32 <= K <= 8192, K % 32 == 0, bits in {4, 6}. */
+ * 64 <= K <= 8192, K % 64 == 0, bits in {4, 6}. */
 convrot_status convrot_gemm_g16_bf16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw,
                                      const uint8_t* f8, const float* s_row, int N, int bits, const uint16_t* bias,
                                      uint16_t* y, hipStream_t stream);

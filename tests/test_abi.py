@@ -38,6 +38,7 @@ def test_g16_validation(L):
     g = L.convrot_gemm_g16_bf16
     assert g(P, P, 8, 512, P, P, P, 16, 8, None, P, None) == BITS
     assert g(P, P, 8, 48, P, P, P, 16, 4, None, P, None) == SHAPE
+    assert g(P, P, 8, 96, P, P, P, 16, 4, None, P, None) == SHAPE  # K a multiple of 64
     assert g(P, P, 0, 512, P, P, P, 16, 4, None, P, None) == SHAPE
     assert g(P, P, 8, 512, P, P, P, 16, 4, P + 4, P, None) == ALIGN
     lin = L.convrot_linear_g16

@@ -131,15 +131,19 @@ __global__ __launch_bounds__(kConvThreads) void quantize_g16_kernel(const uint16
 // Workgroup tile 128 tokens x 128 weight rows, 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), K in steps
 // of 32 (two groups).  Each step is staged in LDS already decoded to fp16 (tokens: code; weights: code * f),
 // double-buffered: the next step's global loads are in flight while the current one is multiplied.
-constexpr int kBM = 128, kBN = 128, kBK = 32;
+#ifndef CRK_G16_BK
+#define CRK_G16_BK 64
+#endif
+constexpr int kBM = 128, kBN = 128, kBK = CRK_G16_BK;
 constexpr int kGemmThreads = 256;
-constexpr int kRowHalves = kBK + 8;  // LDS row pitch (80 bytes) spreads the fragment reads over the banks
+constexpr int kGPT = kBK / 32;        // groups of 16 per thread per step (two threads per row)
+constexpr int kRowHalves = kBK + 8;  // LDS row pitch: the 16-byte pad spreads the fragment reads over the banks
 
 template <int BITS>
 struct StageRegs {
-    uint4 a;                       // 16 token codes
-    uint32_t b[BITS == 6 ? 3 : 2];  // 16 packed weight codes
-    uint32_t f;                     // their E4M3 scale
+    uint4 a[kGPT];                        // 16 token codes per group
+    uint32_t b[kGPT][BITS == 6 ? 3 : 2];  // 16 packed weight codes per group
+    uint32_t f[kGPT];                     // their E4M3 scales
 };
 
 template <int BITS>
@@ -148,19 +152,22 @@ __device__ __forceinline__ void stage_load(StageRegs<BITS>& r, const int8_t* __r
                                            int m0, int n0, int k0) {
     const int t = threadIdx.x, row = t >> 1, hk = t & 1;
     const int m = min(m0 + row, M - 1), n = min(n0 + row, N - 1);  // rows past the end compute unused outputs
-    r.a = *reinterpret_cast<const uint4*>(qx + (int64_t)m * K + k0 + 16 * hk);
-    const int grp = k0 / 16 + hk;
-    if constexpr (BITS == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(qw + (int64_t)n * (K / 2) + 8 * grp);
-        r.b[0] = v.x;
-        r.b[1] = v.y;
-    } else {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(qw + (int64_t)n * (K / 4 * 3) + 12 * grp);
-        r.b[0] = p[0];
-        r.b[1] = p[1];
-        r.b[2] = p[2];
+#pragma unroll
+    for (int u = 0; u < kGPT; ++u) {
+        const int grp = k0 / 16 + kGPT * hk + u;
+        r.a[u] = *reinterpret_cast<const uint4*>(qx + (int64_t)m * K + 16 * grp);
+        if constexpr (BITS == 4) {
+            const uint2 v = *reinterpret_cast<const uint2*>(qw + (int64_t)n * (K / 2) + 8 * grp);
+            r.b[u][0] = v.x;
+            r.b[u][1] = v.y;
+        } else {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(qw + (int64_t)n * (K / 4 * 3) + 12 * grp);
+            r.b[u][0] = p[0];
+            r.b[u][1] = p[1];
+            r.b[u][2] = p[2];
+        }
+        r.f[u] = f8[(int64_t)n * (K / 16) + grp];
     }
-    r.f = f8[(int64_t)n * (K / 16) + grp];
 }
 
 // Decoding to fp16 with integer operations: for a code c in [-2^(b-1), 2^(b-1)), the half whose bits are
@@ -174,11 +181,11 @@ __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(ui
 __device__ __forceinline__ h2 bits_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 
 template <int BITS>
-__device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* As, _Float16* Bs) {
+__device__ __forceinline__ void stage_store_group(const StageRegs<BITS>& r, int u, _Float16* As, _Float16* Bs) {
     const int t = threadIdx.x, row = t >> 1, hk = t & 1;
     uint32_t a[8], b[8];
     // tokens: bytes k and k + 4 of each 8-byte chunk into one register, sign bit flipped (x + 128 in 0..255)
-    const uint32_t aw[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+    const uint32_t aw[4] = {r.a[u].x, r.a[u].y, r.a[u].z, r.a[u].w};
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -186,7 +193,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* 
             const uint32_t x = __builtin_amdgcn_perm(aw[2 * c + 1], aw[2 * c], 0x0c040c00u + (uint32_t)(i | (i << 16)));
             a[4 * c + i] = h2_bits(bits_h2(x ^ 0x64806480u) - h2{(_Float16)1152.0f, (_Float16)1152.0f});
         }
-    const _Float16 fh = (_Float16)e4m3_decode(r.f);  // every E4M3 value is an fp16 value
+    const _Float16 fh = (_Float16)e4m3_decode(r.f[u]);  // every E4M3 value is an fp16 value
     const h2 f2{fh, fh};
     if constexpr (BITS == 4) {
         // word c holds codes 8c..8c+7 as nibbles; (w >> 4i) & 0x000f000f puts codes i and i + 4 in the halves
@@ -194,7 +201,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* 
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t x = (r.b[c] >> (4 * i)) & 0x000f000fu;
+                const uint32_t x = (r.b[u][c] >> (4 * i)) & 0x000f000fu;
                 b[4 * c + i] =
                     h2_bits((bits_h2(x ^ 0x64086408u) - h2{(_Float16)1032.0f, (_Float16)1032.0f}) * f2);
             }
@@ -202,8 +209,8 @@ __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* 
         // code j at bit 6 j of the 96-bit run; alignbit takes a field that straddles two words
         auto field = [&](int j) -> uint32_t {
             const int p = 6 * j, w = p >> 5;
-            const uint32_t hi = w + 1 < 3 ? r.b[w + 1] : 0u;
-            return __builtin_amdgcn_alignbit(hi, r.b[w], (uint32_t)(p & 31)) & 63u;
+            const uint32_t hi = w + 1 < 3 ? r.b[u][w + 1] : 0u;
+            return __builtin_amdgcn_alignbit(hi, r.b[u][w], (uint32_t)(p & 31)) & 63u;
         };
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -214,12 +221,18 @@ __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* 
                     h2_bits((bits_h2(x ^ 0x64206420u) - h2{(_Float16)1056.0f, (_Float16)1056.0f}) * f2);
             }
     }
-    uint32_t* ao = reinterpret_cast<uint32_t*>(As + row * kRowHalves + 16 * hk);
-    uint32_t* bo = reinterpret_cast<uint32_t*>(Bs + row * kRowHalves + 16 * hk);
+    uint32_t* ao = reinterpret_cast<uint32_t*>(As + row * kRowHalves + 16 * (kGPT * hk + u));
+    uint32_t* bo = reinterpret_cast<uint32_t*>(Bs + row * kRowHalves + 16 * (kGPT * hk + u));
     *reinterpret_cast<uint4*>(ao) = make_uint4(a[0], a[1], a[2], a[3]);
     *reinterpret_cast<uint4*>(ao + 4) = make_uint4(a[4], a[5], a[6], a[7]);
     *reinterpret_cast<uint4*>(bo) = make_uint4(b[0], b[1], b[2], b[3]);
     *reinterpret_cast<uint4*>(bo + 4) = make_uint4(b[4], b[5], b[6], b[7]);
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* As, _Float16* Bs) {
+#pragma unroll
+    for (int u = 0; u < kGPT; ++u) stage_store_group<BITS>(r, u, As, Bs);
 }
 
 template <int BITS>
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
         const int buf = kt & 1;
         if (kt + 1 < nk) stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, (kt + 1) * kBK);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < kBK / 16; ++s) {
             // fragment: row lane % 32 of a 32-row block, halves 16 s + 8 (lane / 32) .. + 8
             const int col = 16 * s + 8 * (lane >> 5);
             v8h af[2], bf[2];
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
 hipError_t launch_quantize_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q, uint8_t* f8,
                                float* s_row, hipStream_t st) {
     if (N == 0) return hipSuccess;
-    const size_t lds = sizeof(float) * (size_t)K;
+    const size_t lds = sizeof(float) * (size_t)K;  // the row, at most 32 KiB
     if (bits == 6)
         quantize_g16_kernel<6><<<dim3((unsigned)N), dim3(kConvThreads), lds, st>>>(w, K, group, q, f8, s_row);
     else
