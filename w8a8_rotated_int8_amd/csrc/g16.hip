@@ -129,12 +129,10 @@ __global__ __launch_bounds__(kConvThreads) void quantize_g16_kernel(const uint16
 
 // ---- GEMM + dequant ---------------------------------------------------------------------------------------
 // Workgroup tile 128 tokens x 128 weight rows, 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), K in steps
-// of 32 (two groups).  Each step is staged in LDS already decoded to fp16 (tokens: code; weights: code * f),
-// double-buffered: the next step's global loads are in flight while the current one is multiplied.
-#ifndef CRK_G16_BK
-#define CRK_G16_BK 64
-#endif
-constexpr int kBM = 128, kBN = 128, kBK = CRK_G16_BK;
+// of 64 (four groups; measured faster than 32).  Each step is staged in LDS already decoded to fp16 (tokens:
+// code; weights: code * f), double-buffered: the next step's global loads are in flight while the current one
+// is multiplied.
+constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kGemmThreads = 256;
 constexpr int kGPT = kBK / 32;        // groups of 16 per thread per step (two threads per row)
 constexpr int kRowHalves = kBK + 8;  // LDS row pitch: the 16-byte pad spreads the fragment reads over the banks
