@@ -128,12 +128,14 @@ __global__ __launch_bounds__(kConvThreads) void quantize_g16_kernel(const uint16
 }
 
 // ---- GEMM + dequant ---------------------------------------------------------------------------------------
-// Workgroup tile 128 tokens x 128 weight rows, 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), K in steps
-// of 64 (four groups; measured faster than 32).  Each step is staged in LDS already decoded to fp16 (tokens:
-// code; weights: code * f), double-buffered: the next step's global loads are in flight while the current one
-// is multiplied.
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kGemmThreads = 256;
+// Workgroup tile 256 tokens x 256 weight rows, 8 wavefronts of 64 tokens x 128 rows (2 x 4 blocks of 32 x 32),
+// K in steps of 64 (four groups).  Each step is staged in LDS already decoded to fp16 (tokens: code; weights:
+// code * f), double-buffered (144 KiB): the next step's global loads are in flight while the current one is
+// multiplied.  The 256 x 256 tile measured 18 % faster than 128 x 128 (half the decode and a third less LDS
+// traffic per multiply-add), and K steps of 64 faster than 32.
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kGemmThreads = 512;
+constexpr int kWN = 4;  // 32-row weight blocks per wavefront (wavefront tile 64 tokens x 128 rows)
 constexpr int kGPT = kBK / 32;        // groups of 16 per thread per step (two threads per row)
 constexpr int kRowHalves = kBK + 8;  // LDS row pitch: the 16-byte pad spreads the fragment reads over the banks
 
@@ -241,24 +243,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
                                                                 const float* __restrict__ s_row, int N,
                                                                 const uint16_t* __restrict__ bias,
                                                                 uint16_t* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kRowHalves];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kBN * kRowHalves];
+    extern __shared__ __attribute__((aligned(16))) _Float16 g16_lds[];
+    _Float16* const lds_base = g16_lds;
+    auto Abuf = [&](int b) { return lds_base + b * (kBM * kRowHalves); };
+    auto Bbuf = [&](int b) { return lds_base + 2 * kBM * kRowHalves + b * (kBN * kRowHalves); };
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;  // wm 0..3 (64 tokens), wn 0..1 (128 rows)
     const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
     const int nk = K / kBK;
 
-    v16f acc[2][2];
+    v16f acc[2][kWN];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kWN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     StageRegs<BITS> regs;
     stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, 0);
-    stage_store<BITS>(regs, As[0], Bs[0]);
+    stage_store<BITS>(regs, Abuf(0), Bbuf(0));
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
@@ -267,20 +271,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
         for (int s = 0; s < kBK / 16; ++s) {
             // fragment: row lane % 32 of a 32-row block, halves 16 s + 8 (lane / 32) .. + 8
             const int col = 16 * s + 8 * (lane >> 5);
-            v8h af[2], bf[2];
+            v8h af[2], bf[kWN];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const v8h*>(As[buf] + (wm * 64 + 32 * i + (lane & 31)) * kRowHalves + col);
+                af[i] = *reinterpret_cast<const v8h*>(Abuf(buf) + (wm * 64 + 32 * i + (lane & 31)) * kRowHalves + col);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const v8h*>(Bs[buf] + (wn * 64 + 32 * j + (lane & 31)) * kRowHalves + col);
+            for (int j = 0; j < kWN; ++j)
+                bf[j] = *reinterpret_cast<const v8h*>(Bbuf(buf) + (wn * 128 + 32 * j + (lane & 31)) * kRowHalves + col);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kWN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) stage_store<BITS>(regs, As[buf ^ 1], Bs[buf ^ 1]);
+        if (kt + 1 < nk) stage_store<BITS>(regs, Abuf(buf ^ 1), Bbuf(buf ^ 1));
         __syncthreads();
     }
 
@@ -293,10 +297,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
         if (m >= M) continue;
         const float sm = sx[m];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kWN; ++j)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const int nb = n0 + wn * 64 + 32 * j + 8 * qd + 4 * (lane >> 5);
+                const int nb = n0 + wn * 128 + 32 * j + 8 * qd + 4 * (lane >> 5);
                 uint32_t h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -335,10 +339,17 @@ hipError_t launch_quantize_g16(const uint16_t* w, int N, int K, int group, int b
 hipError_t launch_gemm_g16(const int8_t* qx, const float* sx, int M, int K, const uint8_t* qw, const uint8_t* f8,
                            const float* s_row, int N, int bits, const uint16_t* bias, uint16_t* y, hipStream_t st) {
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(kGemmThreads);
+    constexpr size_t kLds = sizeof(_Float16) * 2 * (kBM + kBN) * kRowHalves;
+    static const hipError_t a6 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_g16_kernel<6>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    static const hipError_t a4 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_g16_kernel<4>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (a6 != hipSuccess) return a6;
+    if (a4 != hipSuccess) return a4;
     if (bits == 6)
-        gemm_g16_kernel<6><<<grid, block, 0, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
+        gemm_g16_kernel<6><<<grid, block, kLds, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
     else
-        gemm_g16_kernel<4><<<grid, block, 0, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
+        gemm_g16_kernel<4><<<grid, block, kLds, st>>>(qx, sx, M, K, qw, f8, s_row, N, bias, y);
     return hipGetLastError();
 }
 
