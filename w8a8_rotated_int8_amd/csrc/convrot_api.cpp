@@ -276,7 +276,7 @@ convrot_status convrot_gemm_g16_bf16(const int8_t* qx, const float* sx, int M, i
                                      uint16_t* y, hipStream_t stream) {
     if (!qx || !sx || !qw || !f8 || !s_row || !y) return CONVROT_ERR_NULL;
     if (bits != 4 && bits != 6) return CONVROT_ERR_BITS;
-    if (M < 1 || N < 1 || K < 64 || K > kMaxRowLen || K % 64 || (M + 127) / 128 > 65535) return CONVROT_ERR_SHAPE;
+    if (M < 1 || N < 1 || K < 64 || K > kMaxRowLen || K % 64 || (M + 255) / 256 > 65535) return CONVROT_ERR_SHAPE;
     if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(f8) || !aligned16(s_row) ||
         !aligned16(y) || (bias && !aligned16(bias)))
         return CONVROT_ERR_ALIGN;
@@ -289,7 +289,7 @@ convrot_status convrot_linear_g16(const uint16_t* x, int M, int K, const uint8_t
                                   void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!x || !qw || !f8 || !s_row || !y) return CONVROT_ERR_NULL;
     if (bits != 4 && bits != 6) return CONVROT_ERR_BITS;
-    if (M < 1 || N < 1 || K < 1 || K > kMaxRowLen || (M + 127) / 128 > 65535) return CONVROT_ERR_SHAPE;
+    if (M < 1 || N < 1 || K < 1 || K > kMaxRowLen || (M + 255) / 256 > 65535) return CONVROT_ERR_SHAPE;
     if (!group_ok(group) || K % group) return CONVROT_ERR_GROUP;  // also makes K a multiple of 64
     if (!aligned16(x) || !aligned16(qw) || !aligned16(f8) || !aligned16(s_row) || !aligned16(y) ||
         (bias && !aligned16(bias)))
