@@ -504,7 +504,7 @@ def main():
 
     sec = ms * 1e-3 / n_layers  # one layer
     tops = layer_ops(s) / sec / 1e12
-    workload = (f"expert-choice W8A8 ConvRot MoE layer T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} "
+    workload = (f"expert-choice W{args.wbits}A8 ConvRot MoE layer T={s.T} d={s.d} E={s.E} I={s.I} C={s.C} "
                 f"(g_gu={s.g_gu}, g_dn={s.g_dn}, {args.wbits}-bit weights)")
     if n_layers > 1:
         workload = f"{n_layers} stacked {workload.replace('layer', 'layers', 1)}, each with its own weights and logits"
