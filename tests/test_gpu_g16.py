@@ -45,7 +45,8 @@ def _check_y(y, ref, aabs, sx, s_row, K, what):
 
 
 @pytest.mark.parametrize("M,K,N,bits,with_bias", [(96, 512, 160, 6, False), (130, 2048, 257, 4, True),
-                                                  (64, 1536, 128, 6, True), (1, 256, 3, 4, False)])
+                                                  (64, 1536, 128, 6, True), (1, 256, 3, 4, False),
+                                                  (300, 8192, 96, 4, False), (257, 256, 513, 6, True)])
 def test_gemm_stage_within_tolerance(M, K, N, bits, with_bias):
     say(f"g16 GEMM M={M} K={K} N={N} bits={bits} bias={with_bias}")
     g = 256 if K % 256 == 0 else 64
@@ -74,19 +75,21 @@ def test_linear_end_to_end(bits):
     _check_y(y, ref, aabs, sx, host(s), K, "linear")
 
 
-@pytest.mark.parametrize("bits", [6, 4])
-def test_full_size_qkv(bits):
-    """The dense qkv projection over 8192 tokens (K = 2048, N = 6144): converter bit for bit in full, the
-    linear's output on 64 sampled token rows (all 6144 columns) against the oracle."""
-    M, K, N, g = synth.DENSE_SHAPES["qkv"]
-    say(f"g16 full-size qkv M={M} K={K} N={N} bits={bits}")
-    x, w, _ = synth.dense_linear_inputs(M, K, N, False)
+@pytest.mark.parametrize("name,bits", [("qkv", 6), ("qkv", 4), ("out", 4)])
+def test_full_size(name, bits):
+    """Dense projections over 8192 tokens (qkv: K = 2048, N = 6144; out: K = N = 2048, group 64, bias):
+    converter bit for bit in full, the linear's output on 64 sampled token rows (all columns) against the
+    oracle."""
+    M, K, N, g = synth.DENSE_SHAPES[name]
+    with_bias = name == "out"
+    say(f"g16 full-size {name} M={M} K={K} N={N} g={g} bits={bits}")
+    x, w, b = synth.dense_linear_inputs(M, K, N, with_bias)
     q, f8, s = cr.convrot_quantize_weights_g16(dev_bf16(w), g, bits)
-    y = cr.convrot_linear_g16(dev_bf16(x), q, f8, s, g, bits)
+    y = cr.convrot_linear_g16(dev_bf16(x), q, f8, s, g, bits, bias=None if b is None else dev_bf16(b))
     torch.cuda.synchronize()
     rq, rf, rs, codes = oracle.quantize_g16(w, g, bits)
     assert np.array_equal(host(q), rq) and np.array_equal(host(f8), rf)
     assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
     rows = np.sort(np.random.default_rng(9).choice(M, 64, replace=False))
-    ref, qx, sx, acc, aabs = oracle.linear_g16(x[rows], g, codes, rf, rs)
+    ref, qx, sx, acc, aabs = oracle.linear_g16(x[rows], g, codes, rf, rs, b)
     _check_y(y[torch.from_numpy(rows).to(DEV)], ref, aabs, sx, rs, K, "full-size linear (sampled rows)")
