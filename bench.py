@@ -75,6 +75,18 @@ def read_traffic():
     return float(t.group(1))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_cores() -> int:
     n = len(os.sched_getaffinity(0))
     omp = os.environ.get("OMP_NUM_THREADS")
@@ -96,7 +108,7 @@ def cpu_baseline(x, lg, w_gu, w_dn, s, n_experts: int, min_seconds: float = 10.0
         dt += time.perf_counter() - t0
         reps += 1
     ops = 6.0 * n_experts * s.C * s.I * s.d * reps
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle",
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"T={s.T} layer restricted to experts 0..{n_experts - 1} (each C={s.C} tokens, full per-expert "
                       f"work), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s, scaled to TOPS"}
 
@@ -112,7 +124,7 @@ def dense_cpu_baseline(x, q, s, g, b, M, K, N, min_seconds: float = 10.0):
         dt += time.perf_counter() - t0
         reps += 1
     ops = 2.0 * M * N * K * reps
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle",
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cpu_cores(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"the whole linear (M={M}, K={K}, N={N}), run {reps} times: {ops / 1e9:.1f} GOP in {dt:.2f} s"}
 
 
@@ -304,7 +316,7 @@ def run_g16(args):
             dt += time.perf_counter() - t0
             reps += 1
         line["cpu_baseline"] = {"value": 2.0 * rows * N * K * reps / dt / 1e12, "unit": "TOPS",
-                                "cores": cpu_cores(), "kind": "oracle",
+                                "cores": cpu_cores(), "kind": "oracle", "cpu": cpu_model(),
                                 "sample": f"the linear on the first {rows} of the {M} token rows (all {N} outputs), "
                                           f"run {reps} times in {dt:.2f} s"}
     print(json.dumps(line), flush=True)
@@ -385,8 +397,8 @@ def run_lora(args):
             dt += time.perf_counter() - t0
             reps += 1
         line["cpu_baseline"] = {"value": N * K * reps / dt / 1e9, "unit": "GB/s", "cores": cpu_cores(),
-                                "kind": "oracle", "sample": f"expert 0 of the set ({N} x {K}), run {reps} times "
-                                                            f"in {dt:.2f} s"}
+                                "kind": "oracle", "cpu": cpu_model(),
+                                "sample": f"expert 0 of the set ({N} x {K}), run {reps} times in {dt:.2f} s"}
     print(json.dumps(line), flush=True)
 
 
