@@ -241,7 +241,8 @@ convrot_status convrot_gemm_g16_bf16(const int8_t* qx, const float* sx, int M, i
                                      const uint8_t* f8, const float* s_row, int N, int bits, const uint16_t* bias,
                                      uint16_t* y, hipStream_t stream);
 
-/* The whole linear: x (device) [M, K] bf16; workspace as convrot_linear_workspace_bytes(M, K). */
+/* The whole linear: x (device) [M, K] bf16; workspace as convrot_linear_workspace_bytes(M, K).  Requires
+ * M, N >= 1, group in {64, 256}, K % group == 0, K <= 8192, bits in {4, 6}. */
 convrot_status convrot_linear_g16(const uint16_t* x, int M, int K, const uint8_t* qw, const uint8_t* f8,
                                   const float* s_row, int N, int group, int bits, const uint16_t* bias, uint16_t* y,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
