@@ -122,6 +122,7 @@ def test_stage_validation(L):
     assert L.convrot_quantize_prerotated(P, 4, 16, 6, P, P, None) == BITS
     assert L.convrot_gemm_i8_i32(P, P, 4, 4, 24, P, None) == SHAPE
     assert L.convrot_gemm_i8_i32(P, P, 4, 4, 140000, P, None) == SHAPE
+    assert L.convrot_gemm_i8_i32(P, P, 4, 4, 131072, P, None) == SHAPE  # K * 128^2 reaches 2^31
     assert L.convrot_gemm_i8_i32(P, None, 4, 4, 32, P, None) == NULL
     assert L.convrot_gemm_w8a8_bf16(P, P, 4, 96, P, P, 8, None, P, None) == SHAPE  # K % 64
     assert L.convrot_gemm_w8a8_bf16(P, P, 0, 128, P, P, 8, None, P, None) == SHAPE

@@ -15,7 +15,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kRotqBesideSoftmaxPct = 25;  // share of the token rows rotated in the softmax launch
 constexpr int kMaxRowLen = 8192;           // rotate/quantise keeps a row in registers of one wavefront
-constexpr int64_t kMaxKInt32 = 133144;     // K * 127^2 < 2^31
+constexpr int64_t kMaxKInt32 = 131056;     // K * 128^2 < 2^31 for any int8 codes (-128 included), K % 16 == 0
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 

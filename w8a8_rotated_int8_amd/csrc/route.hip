@@ -201,6 +201,9 @@ __device__ __forceinline__ int block_excl_sum(int v, int* scratch, int& total) {
 // (# greater keys before it) + min(# equal keys before it, C - # greater keys overall), and both prefixes come
 // from ballots within a round.
 constexpr int kSelV = 8;  // wavefronts per workgroup
+constexpr int kSelBins = 2048;  // radix bins of one pass (11 bits)
+// the bins are cleared with one 16-byte chunk per thread of the workgroup
+static_assert(kSelV * 64 * 4 == kSelBins, "selection workgroup size and bin count are tied");
 
 // Wavefront-wide min / max / sum of a uint32 through DPP (quad permutations and row rotations reduce each
 // 16-lane row) and four lane reads; the result is wave-uniform.
@@ -245,7 +248,7 @@ template <int KR>
 __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ probs_t, int T, int C,
                                                     int32_t* __restrict__ idx, float* __restrict__ wt,
                                                     int32_t* __restrict__ slotmap, int e) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
     __shared__ uint32_t s_red[2 * kSelV];
     __shared__ uint32_t s_bcast[2];
     __shared__ int s_cnt[2 * kSelV];
@@ -313,8 +316,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
         const uint32_t dmask = (1u << width) - 1u;
         hi = shift;
         __syncthreads();  // the previous scan is done with the bins
-#pragma unroll
-        for (int k = 0; k < 2; ++k) reinterpret_cast<uint4*>(hist)[tid + 256 * k] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4*>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);  // one 16-byte chunk per thread
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < KR; ++j)
