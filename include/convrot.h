@@ -22,16 +22,18 @@
  *    Activations get one scale per token (row) computed from the call's own data.
  *  - Product: exact INT32 sum of INT8 x INT8 (|acc| <= K * 127^2, so K <= 133144).
  *  - Dequantisation: bf16_rne( ((float)acc * s_act) * s_w ) [+ (float)bias, added before the rounding].
- *  - SwiGLU: a = bf16_rne( silu(g) * u ), silu(g) = g / (1 + E(-g)), g and u the bf16 gate/up outputs.
+ *  - SwiGLU: a = bf16_rne( silu(g) * u ), silu(g) = g / (1 + E(-g)) (g * E(g) for g < -64, where 1 + E(g)
+ *    is exactly 1), g and u the bf16 gate/up outputs.
  *  - Router: p[t, :] = softmax over experts in fp32 (max-subtracted, E() of the differences, sum in ascending
  *    expert order, one division per entry).  Expert e takes the C tokens with the largest p[:, e], ties to the
  *    lower token index, listed in ascending token order; its gate weight is that p (not renormalised).
  *  - Combine: out[t, :] = bf16_rne( sum over experts e in ascending order that took t of w * (float)z ),
  *    fp32, starting from +0.0f; a token taken by no expert gets +0.
- *  - E(x) is a fixed fp32 exponential: x clamped to [-86, 88]; n = rint(x * log2e); r = fma(-n, ln2_lo,
+ *  - E(x) is a fixed fp32 exponential: x clamped to [-150, 100]; n = rint(x * log2e); r = fma(-n, ln2_lo,
  *    fma(-n, ln2_hi, x)) with ln2_hi = ln 2 rounded to 16 significant bits (Cody-Waite reduction); Taylor
  *    series of e^r through r^7 by Horner's rule in fused multiply-adds (coefficients 1/k! rounded to fp32);
- *    exact scaling by 2^n.  Every other fp32 step above is a separate IEEE operation (no contraction), so
+ *    p * 2^n rounded once (exact when normal), so E underflows through the subnormals to 0 and overflows to
+ *    +inf where the fp32 rounding of e^x does.  Every other fp32 step above is a separate IEEE operation (no contraction), so
  *    results are reproducible bit for bit.
  *
  * Conventions for every call:

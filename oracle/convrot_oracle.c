@@ -37,8 +37,9 @@
  *    (fp32 division, ties to even); an all-zero row has scale 0 and codes 0.  qmax = 127 for INT8,
  *    7 for INT4.  Activations use one scale per token over the whole rotated row.
  *  - Dequantisation: bf16( ((float)acc * s_act) * s_w ), optional bias added in fp32 before rounding.
- *  - silu(g) = g / (1 + E(-g)), where E is the fixed fp32 exponential defined in oracle_exp below
- *    (clamped argument, Cody-Waite reduction, Taylor polynomial, fused multiply-adds as written).
+ *  - silu(g) = g / (1 + E(-g)) (g * E(g) below g = -64, where 1 + E(g) is exactly 1), where E is the
+ *    fixed fp32 exponential defined in oracle_exp below (Cody-Waite reduction, Taylor polynomial, fused
+ *    multiply-adds as written, one rounding of p * 2^n, so it underflows and overflows as e^x does).
  *  - Router: softmax over the experts of each token in fp32 (max-subtracted, E() of the differences,
  *    sum in ascending expert order, one division).  Expert e takes the C tokens with the largest
  *    probability, ties to the lower token index; its list is written in ascending token order and its
@@ -93,23 +94,25 @@ void oracle_bf16_round(const float* in, int64_t n, uint16_t* out) {
 /* ------------------------------------------------------------------------------------------------- */
 /* E(x): the fixed fp32 exponential used by silu and softmax.                                          */
 /*                                                                                                     */
-/* The argument is first clamped to [-86, 88] (outside, E returns the value at the end of the range:   */
-/* about 4.5e-38 below, 1.65e38 above).  Then Cody & Waite's additive range reduction ("Software       */
-/* Manual for the Elementary Functions", 1980): n = rint(x * log2(e)), r = x - n*LN2_HI - n*LN2_LO,     */
-/* where LN2_HI is ln 2 rounded to 16 significant bits (n*LN2_HI is exact for |n| < 256) and LN2_LO =  */
-/* ln 2 - LN2_HI rounded to fp32, each step one fused multiply-add.  e^r comes from its Taylor series   */
-/* through r^7 (terms 1/k! rounded to fp32) evaluated by Horner's rule with fused multiply-adds, and    */
-/* the result is scaled exactly by 2^n.  fmaf and ldexpf are correctly rounded / exact, so this is a   */
-/* fixed sequence of IEEE fp32 operations.                                                             */
+/* Cody & Waite's additive range reduction ("Software Manual for the Elementary Functions", 1980):      */
+/* n = rint(x * log2(e)), r = x - n*LN2_HI - n*LN2_LO, where LN2_HI is ln 2 rounded to 16 significant   */
+/* bits (n*LN2_HI is exact for |n| < 256) and LN2_LO = ln 2 - LN2_HI rounded to fp32, each step one     */
+/* fused multiply-add.  e^r comes from its Taylor series through r^7 (terms 1/k! rounded to fp32)       */
+/* evaluated by Horner's rule with fused multiply-adds, and the result is p * 2^n rounded once to fp32  */
+/* (ldexpf: exact for a normal result, one IEEE rounding for a subnormal one, +inf past the largest    */
+/* finite value).  So E follows e^x into the subnormal range and reaches 0 below about -103.97 and     */
+/* +inf above about 88.72, as the fp32 rounding of e^x does.  The argument is first clamped to          */
+/* [-150, 100]: that keeps |n| < 256 (the reduction stays exact) and changes no result, since e^x       */
+/* already rounds to 0 below -104 and to +inf above 89.                                                 */
 /* ------------------------------------------------------------------------------------------------- */
 
 float oracle_exp(float x) {
     const float log2e = 0x1.715476p+0f;       /* log2(e) rounded to fp32 */
     const float ln2_hi = 0x1.62e4p-1f;        /* 45426 / 65536 = 0.693145751953125 */
     const float ln2_lo = 0x1.7f7d1cp-20f;     /* ln 2 - ln2_hi, rounded to fp32 */
-    if (x < -86.0f) x = -86.0f;
-    if (x > 88.0f) x = 88.0f;
-    float n = rintf(x * log2e);
+    if (x < -150.0f) x = -150.0f;
+    if (x > 100.0f) x = 100.0f;
+    float n = rintf(x * log2e);               /* -216 <= n <= 144 */
     float r = fmaf(-n, ln2_hi, x);
     r = fmaf(-n, ln2_lo, r);
     float p = 1.0f / 5040.0f;                 /* 1/7! */
@@ -120,15 +123,19 @@ float oracle_exp(float x) {
     p = fmaf(p, r, 0.5f);
     p = fmaf(p, r, 1.0f);
     p = fmaf(p, r, 1.0f);
-    return ldexpf(p, (int)n); /* -124 <= n <= 127: a normal result, exact scaling */
+    return ldexpf(p, (int)n);                 /* p * 2^n, rounded once */
 }
 
 void oracle_exp_array(const float* x, int64_t n, float* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp(x[i]);
 }
 
-/* silu(g) = g * sigmoid(g) = g / (1 + e^-g)  [MLX: MoE experts use silu(gate) * up] */
+/* silu(g) = g * sigmoid(g) = g / (1 + e^-g)  [MLX: MoE experts use silu(gate) * up].
+ * Below g = -64, e^-g would overflow fp32 from about -88.7 on while silu(g) is still a normal or
+ * subnormal number; there 1 + e^g rounds to exactly 1 (e^g < 2^-92), so silu(g) = g * e^g, which is
+ * the same function written without the overflow. */
 float oracle_silu(float g) {
+    if (g < -64.0f) return g * oracle_exp(g);
     float e = oracle_exp(-g);
     float den = 1.0f + e;
     return g / den;

@@ -38,26 +38,55 @@ def test_bf16_round_matches_torch(orc):
     assert np.array_equal(ours, ref)
 
 
+def _all_finite_bf16_as_f32():
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    return f[np.isfinite(f)]
+
+
 def test_exp_within_two_ulp_of_libm(orc):
-    x = np.linspace(-86.0, 88.0, 2_000_001, dtype=np.float32)
+    # Every fp32 result, normal and subnormal, is within 2 units in the last place of e^x rounded from
+    # float64: a dense sweep from where e^x rounds to 0 to where it overflows, and every finite bf16 input.
+    x = np.concatenate([np.linspace(-110.0, 95.0, 4_000_001, dtype=np.float32), _all_finite_bf16_as_f32()])
     ours = orc.exp(x)
-    ref = np.exp(x.astype(np.float64)).astype(np.float32)
-    assert _ulp_diff_f32(ours, ref).max() <= 2
+    with np.errstate(over="ignore"):
+        ref = np.exp(x.astype(np.float64)).astype(np.float32)
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[~fin], ref[~fin])  # +inf exactly where e^x overflows fp32
+    assert _ulp_diff_f32(ours[fin], ref[fin]).max() <= 2
     assert orc.exp(np.float32([0.0]))[0] == 1.0
-    # range ends as documented: the argument is clamped to [-86, 88]
-    lo, hi = orc.exp(np.float32([-86.0, 88.0]))
-    assert np.all(orc.exp(np.float32([-86.5, -1000.0, -np.inf])) == lo) and lo > 0
-    assert np.all(orc.exp(np.float32([88.5, 1e30, np.inf])) == hi) and np.isfinite(hi)
+    # underflow through the subnormals: e^-100 is about 3.7e-44, representable only as a subnormal
+    e100 = orc.exp(np.float32([-100.0]))[0]
+    assert 0.0 < e100 < np.finfo(np.float32).tiny and abs(float(e100) - math.exp(-100.0)) <= 2.0 ** -148
+    # the ends: exactly 0 below about -103.97, +inf above about 88.72, also for infinite arguments
+    assert np.all(orc.exp(np.float32([-104.0, -150.0, -1000.0, -np.inf])) == 0.0)
+    assert np.all(np.isposinf(orc.exp(np.float32([88.73, 100.0, 1e30, np.inf]))))
+    assert np.isfinite(orc.exp(np.float32([88.72]))[0])
+
+
+def _silu_fp64(g):
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore", under="ignore"):
+        e = np.exp(-np.abs(g))  # never overflows
+    return np.where(g >= 0, g / (1.0 + e), g * e / (1.0 + e))
 
 
 def test_silu_close_to_fp64(orc):
-    g = np.linspace(-80.0, 80.0, 400001, dtype=np.float32)
+    # within a few ulp of fp64 silu, with an absolute floor for subnormal results: there e^g carries up to
+    # 2 subnormal ulps and the product with g scales that by |g| (plus one rounding of the product)
+    g = np.concatenate([np.linspace(-160.0, 160.0, 800001, dtype=np.float32), _all_finite_bf16_as_f32()])
     ours = orc.silu(g).astype(np.float64)
-    g64 = g.astype(np.float64)
-    ref = g64 / (1.0 + np.exp(-g64))
-    rel = np.abs(ours - ref) / np.maximum(np.abs(ref), 1e-30)
-    assert rel.max() < 5e-7  # a few fp32 ulp
+    ref = _silu_fp64(g)
+    floor = (2.0 * np.abs(g.astype(np.float64)) + 2.0) * 2.0 ** -149
+    assert np.all(np.abs(ours - ref) <= 5e-7 * np.abs(ref) + floor)
     assert orc.silu(np.float32([0.0]))[0] == 0.0
+    # far negative gates stay on the curve instead of saturating: silu(-90) is about -7.3e-38
+    v = orc.silu(np.float32([-90.0, -100.0]))
+    assert v[0] < 0 and abs(v[0] / (-90.0 * math.exp(-90.0)) - 1.0) < 1e-6
+    assert v[1] < 0 and abs(float(v[1]) + 100.0 * math.exp(-100.0)) <= 202 * 2.0 ** -149
+    assert np.all(orc.silu(np.float32([-120.0, -np.finfo(np.float32).max])) == 0.0)
+    big = np.float32([100.0, 3.0e38])
+    assert np.array_equal(orc.silu(big), big)
 
 
 # ---------------------------------------------------------------------------------------------------------
@@ -297,6 +326,25 @@ def test_routing_invariants_and_ties(orc):
     assert idx.size == 16 * 20
     all_idx, _, _ = orc.route(lg, 256)
     assert np.array_equal(all_idx, np.tile(np.arange(256, dtype=np.int32), (16, 1)))
+
+
+@pytest.mark.parametrize("T,E,C", [(96, 4, 10), (300, 8, 37)])
+def test_routing_resolves_logit_gaps_beyond_86_nats(orc, T, E, C):
+    # Expert choice ranks tokens by their probabilities: each expert's list must be the C highest of the
+    # exact (float64) softmax probabilities rounded to fp32, ties to the lower token index; a saturating
+    # exponential would make every such token tie.
+    lg = synth.large_gap_logits(T, E, T + E)
+    idx, wt, p = orc.route(lg, C)
+    l64 = lg.astype(np.float64)
+    p64 = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p64 /= p64.sum(axis=1, keepdims=True)
+    ref32 = p64.astype(np.float32)
+    assert np.all(ref32[:, 1:] < np.finfo(np.float32).tiny * 2 ** 24) and np.all(ref32[:, 1:] > 0)
+    for e in range(E):
+        order = sorted(range(T), key=lambda t: (-float(ref32[t, e]), t))
+        assert idx[e].tolist() == sorted(order[:C])
+        # and the probabilities themselves follow the exact ones into the subnormal range
+        assert np.all(np.abs(p[:, e].astype(np.float64) - p64[:, e]) <= 4e-7 * p64[:, e] + 2.0 ** -148)
 
 
 # ---------------------------------------------------------------------------------------------------------

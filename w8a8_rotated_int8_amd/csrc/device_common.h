@@ -27,15 +27,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// The library's fixed fp32 exponential E(x).  The argument is clamped to [-86, 88]; then Cody-Waite
-// reduction x = n ln2 + r with ln2 split into a 16-significant-bit head (n * head exact for |n| < 256) and an
-// fp32 tail (one fused multiply-add each), e^r from the Taylor series through r^7 (coefficients 1/k! rounded to
-// fp32) by Horner's rule in fused multiply-adds, and an exact scale by 2^n (v_ldexp_f32).
+// The library's fixed fp32 exponential E(x): Cody-Waite reduction x = n ln2 + r with ln2 split into a
+// 16-significant-bit head (n * head exact for |n| < 256) and an fp32 tail (one fused multiply-add each), e^r
+// from the Taylor series through r^7 (coefficients 1/k! rounded to fp32) by Horner's rule in fused
+// multiply-adds, and p * 2^n rounded once: exact scaling for a normal result; for a subnormal one (n < -126)
+// an exact scale by 2^(n+100) and one IEEE multiply by 2^-100, so the single rounding does not depend on how
+// the scaling instruction treats subnormal results.  E therefore underflows through the subnormals to 0 below
+// about -103.97 and overflows to +inf above about 88.72, as the fp32 rounding of e^x does.  The argument is
+// clamped to [-150, 100] first, which keeps |n| < 256 and changes no result.
 __device__ __forceinline__ float exp_fixed(float x) {
     const float kLog2e = 0x1.715476p+0f;
     const float kLn2Hi = 0x1.62e4p-1f;
     const float kLn2Lo = 0x1.7f7d1cp-20f;
-    x = __builtin_amdgcn_fmed3f(x, -86.0f, 88.0f);
+    x = __builtin_amdgcn_fmed3f(x, -150.0f, 100.0f);
     const float n = rintf(x * kLog2e);
     float r = __builtin_fmaf(-n, kLn2Hi, x);
     r = __builtin_fmaf(-n, kLn2Lo, r);
@@ -47,11 +51,15 @@ __device__ __forceinline__ float exp_fixed(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_amdgcn_ldexpf(p, (int)n);
+    const int ni = (int)n;
+    const bool sub = ni < -126;
+    return __builtin_amdgcn_ldexpf(p, sub ? ni + 100 : ni) * (sub ? 0x1p-100f : 1.0f);
 }
 
-// silu(g) = g / (1 + E(-g))
+// silu(g) = g / (1 + E(-g)); below g = -64, where 1 + E(g) is exactly 1 in fp32, the same value is g * E(g),
+// which does not overflow.
 __device__ __forceinline__ float silu_fixed(float g) {
+    if (g < -64.0f) return g * exp_fixed(g);
     float e = exp_fixed(-g);
     float den = 1.0f + e;
     return g / den;

@@ -96,6 +96,15 @@ def logits(seed_base: int, T: int, E: int) -> np.ndarray:
     return _rng(seed_base + ROLE_LOGITS).standard_normal((T, E), dtype=np.float32)
 
 
+def large_gap_logits(T: int, E: int, seed: int) -> np.ndarray:
+    """Router logits [T, E] whose gaps to each token's maximum are 86 to 100 nats, on a grid of 0.25 nats
+    (probabilities 4.5e-38 down to 3.7e-44, mostly subnormal in fp32; distinct gaps stay tens of subnormal
+    units apart, equal gaps tie exactly).  Expert 0 holds every token's maximum, 0."""
+    lg = -(86.0 + 0.25 * _rng(seed).integers(0, 57, size=(T, E))).astype(np.float32)
+    lg[:, 0] = 0.0
+    return lg
+
+
 def linear_inputs(cfg: int = 0, M=None, K=None, N=None, n_outlier=None):
     """x [M, K] and W [N, K] (bf16 bits) for the single-linear case."""
     c = dict(LINEAR_CFG)
