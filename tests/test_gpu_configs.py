@@ -6,7 +6,8 @@ gate/up + SwiGLU rows, the hidden-row codes, the down rows and the combined outp
 its own from the oracle's inputs, so a mismatch names the stage.  Bar: bit-exact for codes, scales and routing;
 BF16 within 1e-2 relative (and, the arithmetic being fully specified, expected bit-identical).
 
-  * T = 2048, C = 64 and T = 8192, C = 256 layers (64 experts, d = 2048, I = 1536), host-generated inputs;
+  * T = 2048, C = 64, T = 4096, C = 128 and T = 8192, C = 256 layers (64 experts, d = 2048, I = 1536),
+    host-generated inputs;
   * the 29-layer stack: layers 0 and 28 with 8-bit weights and layer 0 with 4-bit weights (weights drawn on the
     GPU by torch's generator, copied to the host for the oracle);
   * dense W8A8 ConvRot linears over the same T = 8192 tokens (fused qkv, an FFN-down-like [2048, 8192] and the
@@ -85,6 +86,17 @@ def test_full_size_layer(cfg, bits):
     what = f"config {cfg} T={s.T} C={s.C} bits={bits}"
     say(f"{what}: generating inputs")
     x, lg, w_gu, w_dn = synth.moe_inputs(cfg)
+    _check_layer(x, lg, dev_bf16(w_gu), dev_bf16(w_dn), w_gu, w_dn, s, bits, what)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_layer_T4096_C128(bits):
+    """A 724x724-image-sized layer at capacity factor 2 (T = 4096, C = 128): the GEMMs' 128-row tile at full
+    expert shapes."""
+    s = synth.MoEShape(T=4096, d=2048, E=64, I=1536, C=128)
+    what = f"T={s.T} C={s.C} bits={bits}"
+    say(f"{what}: generating inputs")
+    x, lg, w_gu, w_dn = synth.moe_inputs(2, s, seed_base=6000)
     _check_layer(x, lg, dev_bf16(w_gu), dev_bf16(w_dn), w_gu, w_dn, s, bits, what)
 
 

@@ -83,8 +83,8 @@ def test_rotq_bit_exact(g, K, rows):
     assert np.array_equal(host(q), rq)
 
 
-@pytest.mark.parametrize("g,K", [(64, 512), (64, 1536), (64, 3072), (64, 4096), (256, 2048), (256, 4096),
-                                 (256, 8192)])
+@pytest.mark.parametrize("g,K", [(64, 512), (64, 1024), (64, 1536), (64, 3072), (64, 4096), (256, 2048),
+                                 (256, 4096), (256, 8192)])
 @pytest.mark.parametrize("rows", [1, 7, 37])
 def test_rotq_codes_only_bit_exact(g, K, rows):
     """The codes-only path (no rotated values requested; the layer's own path), including rows whose scale
@@ -173,7 +173,9 @@ def test_weight_converter_rejects_nonfinite():
 
 @pytest.mark.parametrize("M,K,N,g,with_bias", [(64, 512, 256, 64, False), (64, 512, 256, 64, True),
                                                (37, 768, 77, 256, False), (1, 256, 1, 64, True),
-                                               (300, 2048, 300, 256, True)])
+                                               (300, 2048, 300, 256, True),
+                                               # 65..128 rows: the GEMM's 128-row tile
+                                               (100, 512, 300, 64, True), (128, 1024, 256, 256, False)])
 def test_linear_bit_exact(M, K, N, g, with_bias):
     say(f"linear M={M} K={K} N={N} g={g} bias={with_bias}")
     x, w = synth.linear_inputs(0, M=M, K=K, N=N, n_outlier=max(1, K // 128))
@@ -226,7 +228,11 @@ def test_lora_requant_bit_exact(E, N, K, g, rank, alpha):
 # ----------------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,E,C", [(300, 16, 1), (300, 16, 17), (300, 16, 300), (2048, 64, 64), (5000, 8, 1234),
-                                   (1001, 48, 100), (8192, 64, 256), (13000, 16, 777), (20000, 8, 5000)])
+                                   (1001, 48, 100), (8192, 64, 256), (13000, 16, 777), (20000, 8, 5000),
+                                   # more than 64 experts: the one-thread-per-token softmax
+                                   (500, 96, 50), (70, 80, 70),
+                                   # more than 32768 tokens: the selection that re-reads its keys each pass
+                                   (40000, 4, 3000), (33000, 2, 1)])
 def test_route_from_logits_bit_exact(T, E, C):
     say(f"route T={T} E={E} C={C}")
     lg = synth.logits(T + E, T, E)
@@ -236,6 +242,20 @@ def test_route_from_logits_bit_exact(T, E, C):
     assert np.array_equal(host(p).view(np.uint32), rp.view(np.uint32))
     assert np.array_equal(host(idx), ridx)
     assert np.array_equal(host(wt).view(np.uint32), rwt.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,E,C", [(96, 4, 10), (300, 8, 37), (5000, 64, 100), (40000, 4, 999), (400, 72, 40)])
+def test_route_large_logit_gaps_bit_exact(T, E, C):
+    """Gaps of 86 to 100 nats to the token's maximum: the exponential underflows into the subnormals, the
+    divisions take subnormal numerators, and the selection ranks subnormal probabilities."""
+    say(f"route large gaps T={T} E={E} C={C}")
+    lg = synth.large_gap_logits(T, E, 40 + T + E)
+    idx, wt, p = cr.moe_route_expert_choice(dev(lg), C, want_probs=True)
+    ridx, rwt, rp = oracle.route(lg, C)
+    assert np.array_equal(host(p).view(np.uint32), rp.view(np.uint32))
+    assert np.array_equal(host(idx), ridx)
+    assert np.array_equal(host(wt).view(np.uint32), rwt.view(np.uint32))
+    assert np.count_nonzero((rp[:, 1:] > 0) & (rp[:, 1:] < np.finfo(np.float32).tiny)) > T  # subnormals hit
 
 
 def test_route_from_probs_with_heavy_ties():
@@ -263,6 +283,16 @@ SMALL = [
     # d a multiple of 8 g_gu: the token rotate+quantise rides in the routing launches (rows split between them)
     synth.MoEShape(T=300, d=512, E=8, I=128, C=50, g_gu=64, g_dn=64),
     synth.MoEShape(T=3, d=512, E=2, I=64, C=2, g_gu=64, g_dn=64),
+    # 65..128 slots per expert: the GEMMs' 128-row tile (both epilogues, both weight widths)
+    synth.MoEShape(T=300, d=512, E=4, I=128, C=100),
+    synth.MoEShape(T=256, d=512, E=3, I=192, C=128, g_gu=64, g_dn=64),
+    # the routing launches' rotate+quantise with 4 and 2 register rounds per lane, and the selection with 2 and 8
+    # key rounds per lane (T up to 4096, up to 16384)
+    synth.MoEShape(T=3000, d=2048, E=4, I=64, C=20, g_gu=64, g_dn=64),
+    synth.MoEShape(T=10000, d=1024, E=4, I=64, C=50, g_gu=64, g_dn=64),
+    synth.MoEShape(T=500, d=4096, E=2, I=64, C=10, g_gu=256, g_dn=64),
+    # more than 64 experts: softmax, rotate+quantise and selection as separate launches
+    synth.MoEShape(T=200, d=256, E=80, I=64, C=5, g_gu=64, g_dn=64),
 ]
 
 
@@ -329,3 +359,57 @@ def test_single_expert_ffn_config1():
     assert np.array_equal(host(idx), ref["idx"]) and np.all(host(wt) == 1.0)
     exact = assert_bf16_within(host_bf16(out), ref["out"], what="config 1 out")
     assert exact == 1.0
+
+
+def test_moe_forward_without_routing_outputs():
+    """idx_out / wt_out NULL: the forward keeps the routing in its workspace."""
+    shape = SMALL[5]
+    say(f"moe forward, routing outputs NULL {shape}")
+    x, lg, w, ref = _layer(shape, 8, 30000)
+    out, idx, wt = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w, want_routing=False)
+    assert idx is None and wt is None
+    assert np.array_equal(host_bf16(out), ref["out"])
+
+
+def test_moe_forward_large_logit_gaps():
+    """The whole layer with router logits 86 to 100 nats below each token's maximum (subnormal probabilities
+    weight the combine)."""
+    shape = SMALL[5]
+    say(f"moe forward, large logit gaps {shape}")
+    x, _, w_gu, w_dn = synth.moe_inputs(2, shape, seed_base=31000)
+    lg = synth.large_gap_logits(shape.T, shape.E, 31004)
+    q_gu, s_gu = oracle.quantize_weights(w_gu, shape.g_gu, 8)
+    q_dn, s_dn = oracle.quantize_weights(w_dn, shape.g_dn, 8)
+    ref = oracle.moe_forward(x, lg, shape.C, q_gu, s_gu, shape.g_gu, q_dn, s_dn, shape.g_dn, 8)
+    w = cr.quantize_moe_weights(dev_bf16(w_gu), dev_bf16(w_dn), shape.g_gu, shape.g_dn, 8)
+    out, idx, wt = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w)
+    assert np.array_equal(host(idx), ref["idx"])
+    assert np.array_equal(host(wt).view(np.uint32), ref["wt"].view(np.uint32))
+    assert np.array_equal(host_bf16(out), ref["out"])
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gateup_swiglu_far_gates(bits):
+    """Gate scales stretched so the dequantised gates reach +-1e4: the epilogue evaluates silu for every gate
+    outside its LDS window, including gates below -64 (silu as g * E(g)), below -88.7 (where E(-g) overflows)
+    and below -104 (silu underflows to -0)."""
+    shape = synth.MoEShape(T=96, d=512, E=4, I=128, C=24)
+    say(f"gate/up far gates {shape} bits={bits}")
+    x, lg, w_gu, w_dn = synth.moe_inputs(2, shape, seed_base=32000)
+    w = cr.quantize_moe_weights(dev_bf16(w_gu), dev_bf16(w_dn), shape.g_gu, shape.g_dn, bits)
+    rng = np.random.default_rng(5)
+    s_gu = host(w.s_gu).copy()
+    s_gu[:, :shape.I] *= (10.0 ** rng.uniform(0.0, 4.5, (shape.E, shape.I))).astype(np.float32)
+    w.s_gu = dev(s_gu)
+    q_gu = untile_codes(host(w.q_gu), shape.E, 2 * shape.I, shape.d, bits)
+    qx, sx = oracle.rotq_rows(x, shape.g_gu)
+    idx, _, _ = oracle.route(lg, shape.C)
+    packed = q_gu if bits == 8 else oracle.pack_int4(q_gu)
+    ref = oracle.moe_gateup(qx, sx, idx, packed, s_gu, bits)
+    a = cr.moe_gateup_swiglu(dev(qx), dev(sx), dev(idx), w)
+    assert np.array_equal(host_bf16(a), ref)
+    # the gates really reach the far ranges
+    g = np.concatenate([oracle.gemm_i8_i32(qx[idx[e]], q_gu[e, :shape.I]).astype(np.float64)
+                        * sx[idx[e]][:, None] * s_gu[e, :shape.I][None, :] for e in range(shape.E)])
+    for lo, hi in ((-np.inf, -104.0), (-104.0, -88.8), (-88.7, -64.0), (88.8, np.inf)):
+        assert np.count_nonzero((g > lo) & (g < hi)) > 10, (lo, hi)

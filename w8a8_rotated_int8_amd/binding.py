@@ -17,7 +17,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconvrot_amd.so")
+# CONVROT_AMD_LIB names another build of the same sources (the host-sanitizer build of tests/sanitize.py)
+LIB_PATH = os.environ.get("CONVROT_AMD_LIB") or os.path.join(_HERE, "libconvrot_amd.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "convrot.h")
 PROBES_HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "convrot_probes.h")
 
@@ -215,14 +216,16 @@ def moe_expert_choice_workspace_bytes(T: int, C: int, w: MoeWeights) -> int:
 
 
 def moe_expert_choice_forward(x, router_logits, C: int, w: MoeWeights, out=None, idx_out=None, wt_out=None,
-                              ws=None, stream=None):
-    """Routed-expert MoE layer.  Returns (out [T, d] bf16, idx [E, C] int32, wt [E, C] fp32)."""
+                              ws=None, stream=None, want_routing: bool = True):
+    """Routed-expert MoE layer.  Returns (out [T, d] bf16, idx [E, C] int32, wt [E, C] fp32); with
+    want_routing=False and no idx_out / wt_out given, the routing outputs are not written (NULL) and come back
+    as None."""
     T, d = x.shape
     if out is None:
         out = _empty((T, d), torch.bfloat16, x)
-    if idx_out is None:
+    if idx_out is None and want_routing:
         idx_out = _empty((w.E, C), torch.int32, x)
-    if wt_out is None:
+    if wt_out is None and want_routing:
         wt_out = _empty((w.E, C), torch.float32, x)
     cw = w.c_struct()
     nbytes = lib().moe_expert_choice_workspace_bytes(T, C, ctypes.byref(cw))
