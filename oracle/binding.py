@@ -22,7 +22,8 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "convrot_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# CONVROT_ORACLE_LIB names another build of the same source (the sanitizer pass in tests/sanitize.py)
+_LIB = os.environ.get("CONVROT_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 

@@ -17,7 +17,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # every fp32 expression is evaluated as written: no fused multiply-add, no packed fp32 math
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wextra", "-Werror", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + BUILD,
 ]
