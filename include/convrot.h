@@ -174,6 +174,23 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
                                          const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
                                          float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Size of the static scratch the allocation-free forward uses: 192 MiB per GPU (the T = 8192, C = 256 layer
+ * with E = 64, d = 2048, I = 1536 takes 163.8 MB of it). */
+#define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): moe_expert_choice_forward with the workspace taken from a static device array of
+ * CONVROT_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process ends.
+ * Arguments, steps, results and errors are those of moe_expert_choice_forward; a call whose workspace
+ * (moe_expert_choice_workspace_bytes) exceeds the scratch returns CONVROT_ERR_WORKSPACE and writes nothing.
+ * The first call on a device looks up that device's scratch address once (a HIP runtime call, no
+ * allocation); no call allocates or frees memory.  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents (nothing in it needs to start cleared): calls that overlap on one GPU, from
+ * several streams or threads, race and give undefined results. */
+convrot_status moe_expert_choice_forward_noalloc(const uint16_t* x, int T, const float* router_logits, int C,
+                                                 const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                                 float* wt_out, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------------- */
 /* Stage entry points: each step of the forward on its own, so that every stage can be checked exactly     */
 /* given identical inputs.  Same kernels as the forward.                                                   */
@@ -193,8 +210,8 @@ convrot_status convrot_quantize_prerotated(const float* r, int64_t rows, int K, 
                                            float* s_out, hipStream_t stream);
 
 /* acc_out[M, N] = a[M, K] . b[N, K]^T exactly in int32 (both row-major int8), with the same INT8 MFMA main
- * loop as the layer (B fetched row-major instead of tiled).  Requires M, N >= 1, 16 <= K <= 133144,
- * K % 16 == 0. */
+ * loop as the layer (B fetched row-major instead of tiled).  Requires M, N >= 1, 16 <= K <= 131056,
+ * K % 16 == 0 (K * 128^2 < 2^31 for any int8 codes). */
 convrot_status convrot_gemm_i8_i32(const int8_t* a, const int8_t* b, int M, int N, int K, int32_t* acc_out,
                                    hipStream_t stream);
 

@@ -18,7 +18,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
@@ -142,3 +142,17 @@ def test_stage_validation(L):
     nb = L.moe_combine_workspace_bytes(100, 8)
     assert L.moe_combine(P, P, P, 100, 8, 10, 12, P, P, nb, None) == SHAPE
     assert L.moe_combine(P, P, P, 100, 8, 10, 64, P, P, nb - 1, None) == WS
+
+
+def test_moe_forward_noalloc_validation(L):
+    """The allocation-free forward validates like the forward and rejects workspaces beyond its static
+    scratch before any HIP call."""
+    f = L.moe_expert_choice_forward_noalloc
+    w = _weights()
+    need = L.moe_expert_choice_workspace_bytes(8192, 256, ctypes.byref(w))
+    assert need <= cr.NOALLOC_SCRATCH_BYTES < L.moe_expert_choice_workspace_bytes(8192, 512, ctypes.byref(w))
+    assert f(P, 8192, P, 512, ctypes.byref(w), P, None, None, None) == WS
+    assert f(None, 8192, P, 256, ctypes.byref(w), P, None, None, None) == NULL
+    assert f(P, 8192, P, 8193, ctypes.byref(w), P, None, None, None) == SHAPE
+    assert f(P, 8192, P, 256, ctypes.byref(_weights(group_gu=128)), P, None, None, None) == GROUP
+    assert f(P, 8192, P, 256, ctypes.byref(w), P + 4, None, None, None) == ALIGN

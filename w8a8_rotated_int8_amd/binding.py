@@ -48,6 +48,7 @@ _SIGS = {
     "convrot_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
     "moe_expert_choice_workspace_bytes": (_sz, [_i, _i, ctypes.POINTER(ConvrotMoeWeightsC)]),
     "moe_expert_choice_forward": (_i, [_p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_choice_forward_noalloc": (_i, [_p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p, _p, _p]),
     "convrot_rotq_rows": (_i, [_p, _i64, _i, _i, _p, _p, _p, _p]),
     "convrot_quantize_prerotated": (_i, [_p, _i64, _i, _i, _p, _p, _p]),
     "convrot_gemm_i8_i32": (_i, [_p, _p, _i, _i, _i, _p, _p]),
@@ -233,6 +234,21 @@ def moe_expert_choice_forward(x, router_logits, C: int, w: MoeWeights, out=None,
     _check("moe_expert_choice_forward", lib().moe_expert_choice_forward(
         _ptr(x), T, _ptr(router_logits), C, ctypes.byref(cw), _ptr(out), _ptr(idx_out), _ptr(wt_out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+    return out, idx_out, wt_out
+
+
+NOALLOC_SCRATCH_BYTES = 192 << 20  # CONVROT_NOALLOC_SCRATCH_BYTES
+
+
+def moe_expert_choice_forward_noalloc(x, router_logits, C: int, w: MoeWeights, out, idx_out=None, wt_out=None,
+                                      stream=None):
+    """The forward with the library's static per-GPU scratch as its workspace (the C entry point allocates
+    nothing; `out` and the optional routing outputs are the caller's)."""
+    T, _ = x.shape
+    cw = w.c_struct()
+    _check("moe_expert_choice_forward_noalloc", lib().moe_expert_choice_forward_noalloc(
+        _ptr(x), T, _ptr(router_logits), C, ctypes.byref(cw), _ptr(out), _ptr(idx_out), _ptr(wt_out),
+        _stream(stream)))
     return out, idx_out, wt_out
 
 

@@ -3,6 +3,7 @@
 // no device memory; the caller passes the workspace.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -137,6 +138,78 @@ crk::GemmProblem down_problem(const int8_t* qa, const float* sa, int C, const co
         const hipError_t crk_e_ = (expr);               \
         if (crk_e_ != hipSuccess) return CONVROT_ERR_HIP; \
     } while (0)
+
+convrot_status check_forward(const uint16_t* x, int T, const float* router_logits, int C,
+                              const convrot_moe_weights* w, const uint16_t* out, const int32_t* idx_out,
+                              const float* wt_out) {
+    if (!x || !router_logits || !out) return CONVROT_ERR_NULL;
+    convrot_status st = check_weights(w);
+    if (st != CONVROT_OK) return st;
+    st = check_tc(T, C, w->E);
+    if (st != CONVROT_OK) return st;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(out) || (idx_out && !aligned16(idx_out)) ||
+        (wt_out && !aligned16(wt_out)))
+        return CONVROT_ERR_ALIGN;
+    return CONVROT_OK;
+}
+
+// The forward's launch sequence on a validated call; ws holds at least plan_moe(T, C, w) bytes.  Every
+// workspace byte a launch reads was written by an earlier launch of the same call, so ws need not start
+// cleared.
+convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_logits, int C,
+                               const convrot_moe_weights& w, uint16_t* out, int32_t* idx_out, float* wt_out,
+                               void* ws, hipStream_t stream) {
+    MoeBuffers b;
+    plan_moe(ws, T, C, w, &b);
+    int32_t* idx = idx_out ? idx_out : b.idx;
+    float* wt = wt_out ? wt_out : b.wt;
+    const int64_t S = (int64_t)w.E * C;
+
+    // The token rotate+quantise does not depend on the routing.  Where the shapes allow, its rows are shared
+    // between the softmax launch and the selection launch, both short and latency-bound, so both fill the chip.
+    const int64_t t1 = (int64_t)T * kRotqBesideSoftmaxPct / 100;
+    const bool split = w.E <= 64 && crk::select_rotq_supported(T, w.E, w.d, w.group_gu);
+    if (split) {
+        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, x, w.d, w.group_gu, b.qx, b.sx, t1,
+                                         stream));
+        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slotmap, x, w.d, w.group_gu, b.qx, b.sx,
+                                        t1, stream));
+    } else {
+        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, stream));
+        CRK_TRY(crk::launch_rotq_act(x, T, w.d, w.group_gu, b.qx, b.sx, nullptr, stream));
+        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, stream));
+    }
+    CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, w, b.a), stream));
+    CRK_TRY(crk::launch_rotq_act(b.a, S, w.I, w.group_dn, b.qa, b.sa, nullptr, stream));
+    CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, w, b.z), stream));
+    CRK_TRY(crk::launch_combine(b.z, b.slotmap, wt, T, w.E, C, w.d, out, stream));
+    return CONVROT_OK;
+}
+
+// Scratch of the allocation-free forward: one array per GPU, allocated with the code object when the library
+// is loaded on that GPU and held until the process ends.  Its name is a host-side stand-in; host code uses
+// only the device address that hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        // several threads may race here; each stores the same address
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -312,42 +385,22 @@ size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights
 convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* router_logits, int C,
                                          const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
                                          float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (!x || !router_logits || !out) return CONVROT_ERR_NULL;
-    convrot_status st = check_weights(w);
+    const convrot_status st = check_forward(x, T, router_logits, C, w, out, idx_out, wt_out);
     if (st != CONVROT_OK) return st;
-    st = check_tc(T, C, w->E);
-    if (st != CONVROT_OK) return st;
-    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(out) || (idx_out && !aligned16(idx_out)) ||
-        (wt_out && !aligned16(wt_out)))
-        return CONVROT_ERR_ALIGN;
     if (!ws || ws_bytes < plan_moe(nullptr, T, C, *w, nullptr)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
+    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, stream);
+}
 
-    MoeBuffers b;
-    plan_moe(ws, T, C, *w, &b);
-    int32_t* idx = idx_out ? idx_out : b.idx;
-    float* wt = wt_out ? wt_out : b.wt;
-    const int64_t S = (int64_t)w->E * C;
-
-    // The token rotate+quantise does not depend on the routing.  Where the shapes allow, its rows are shared
-    // between the softmax launch and the selection launch, both short and latency-bound, so both fill the chip.
-    const int64_t t1 = (int64_t)T * kRotqBesideSoftmaxPct / 100;
-    const bool split = w->E <= 64 && crk::select_rotq_supported(T, w->E, w->d, w->group_gu);
-    if (split) {
-        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w->E, b.probs_t, x, w->d, w->group_gu, b.qx, b.sx, t1,
-                                         stream));
-        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w->E, C, idx, wt, b.slotmap, x, w->d, w->group_gu, b.qx, b.sx,
-                                        t1, stream));
-    } else {
-        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w->E, b.probs_t, nullptr, stream));
-        CRK_TRY(crk::launch_rotq_act(x, T, w->d, w->group_gu, b.qx, b.sx, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w->E, C, idx, wt, b.slotmap, stream));
-    }
-    CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, *w, b.a), stream));
-    CRK_TRY(crk::launch_rotq_act(b.a, S, w->I, w->group_dn, b.qa, b.sa, nullptr, stream));
-    CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, *w, b.z), stream));
-    CRK_TRY(crk::launch_combine(b.z, b.slotmap, wt, T, w->E, C, w->d, out, stream));
-    return CONVROT_OK;
+convrot_status moe_expert_choice_forward_noalloc(const uint16_t* x, int T, const float* router_logits, int C,
+                                                 const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                                 float* wt_out, hipStream_t stream) {
+    const convrot_status st = check_forward(x, T, router_logits, C, w, out, idx_out, wt_out);
+    if (st != CONVROT_OK) return st;
+    if (plan_moe(nullptr, T, C, *w, nullptr) > CONVROT_NOALLOC_SCRATCH_BYTES) return CONVROT_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (scratch_of_current_device(&ws) != hipSuccess) return CONVROT_ERR_HIP;
+    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, stream);
 }
 
 convrot_status convrot_rotq_rows(const uint16_t* x, int64_t rows, int K, int group, int8_t* q_out, float* s_out,
