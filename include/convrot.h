@@ -125,9 +125,15 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
 /* Single W8A8 ConvRot linear  (model card "Quantization": W8A8 ConvRot linear with BF16 outputs)          */
 /* ---------------------------------------------------------------------------------------------------- */
 
-/* LoRA patch of quantised weights, re-quantised with random rounding ("NitroFusion2 for ComfyUI", "Why a
+/* Rounding of the LoRA re-quantisation ("XB_UNetLoaderINTROCm", "Inputs that matter": the loader's two LoRA
+ * modes).  RANDOM: the stochastic mode, random-rounding the patched values.  NEAREST: the dynamic mode, which
+ * re-quantises each patched layer: the weight quantiser's nearest rounding (ties to even). */
+typedef enum convrot_rounding { CONVROT_ROUND_RANDOM = 0, CONVROT_ROUND_NEAREST = 1 } convrot_rounding;
+
+/* LoRA patch of quantised weights, re-quantised with fresh scales ("NitroFusion2 for ComfyUI", "Why a
  * step-1 file": a LoRA on a quantised file is re-quantised with fresh scales and random rounding;
- * "XB_UNetLoaderINTROCm", "Inputs that matter": a stochastic LoRA mode bakes LoRAs in at load).
+ * "XB_UNetLoaderINTROCm", "Inputs that matter": a stochastic LoRA mode bakes LoRAs in at load, a dynamic one
+ * re-quantises per layer).
  * q_in (device) [E, N, K] int8 row-major codes and s_in (device) [E, N] scales of weights quantised with
  * `group` (convrot_quantize_weights, CONVROT_LAYOUT_ROWMAJOR, 8 bits); lora_b (device) [E, N, rank] and
  * lora_a (device) [E, rank, K] bf16, the LoRA factors in the original basis (both may be NULL when rank is 0);
@@ -135,13 +141,16 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
  * convrot_weight_bytes(E, N, K, 8, layout) bytes) and s_out (device) [E, N].
  * Per row, in the rotated basis: V = (float)q * s + rotate(alpha * lora_b . lora_a) (delta summed over the
  * rank in ascending order in fp32, then rotated like the weights); scale = max|V| / 127; t = V / scale;
- * code = floor(t), plus 1 when u < t - floor(t), clamped to +-127, where u is the top 24 bits (times 2^-24)
- * of word k % 4 of Philox4x64-10 (Salmon et al., SC 2011) at counter ((e N + n) K/4 + k/4, 0, 0, 0), key
- * (seed, 0).  Deterministic for a given seed.  Requires E, N >= 1, K <= 8192, K % group == 0, group 64 or
- * 256, 0 <= rank <= 4096, alpha finite, q_in, lora_a and q_out 16-byte aligned; errors write nothing. */
+ * rounding CONVROT_ROUND_RANDOM: code = floor(t), plus 1 when u < t - floor(t), clamped to +-127, where u is
+ * the top 24 bits (times 2^-24) of word k % 4 of Philox4x64-10 (Salmon et al., SC 2011) at counter
+ * ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0); deterministic for a given seed.  CONVROT_ROUND_NEAREST:
+ * code = clamp(rint(t), -127, 127) (seed unused).  A zero row gets scale 0 and codes 0 in both.
+ * Requires E, N >= 1, K <= 8192, K % group == 0, group 64 or 256, 0 <= rank <= 4096, alpha finite, rounding
+ * one of the two modes (CONVROT_ERR_SHAPE otherwise), q_in, lora_a and q_out 16-byte aligned; errors write
+ * nothing. */
 convrot_status convrot_requantize_lora(const int8_t* q_in, const float* s_in, int E, int N, int K, int group,
                                        const uint16_t* lora_b, const uint16_t* lora_a, int rank, float alpha,
-                                       uint64_t seed, int layout, int8_t* q_out, float* s_out,
+                                       uint64_t seed, int rounding, int layout, int8_t* q_out, float* s_out,
                                        hipStream_t stream);
 
 /* Bytes of workspace convrot_linear_w8a8 needs for an [M, K] input. */

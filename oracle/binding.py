@@ -69,7 +69,7 @@ def _declare(lib):
         "oracle_unpack_int4": (None, [_p, _i64, _i, _p]),
         "oracle_quantize_weights": (_i, [_p, _i, _i, _i, _i, _i, _p, _p]),
         "oracle_philox4x64_10": (None, [_p, _p, _p]),
-        "oracle_requantize_lora": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _i, ctypes.c_float, ctypes.c_uint64, _p,
+        "oracle_requantize_lora": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _i, ctypes.c_float, ctypes.c_uint64, _i, _p,
                                         _p]),
         "oracle_gemm_i8_i32": (None, [_p, _p, _i, _i, _i, _p]),
         "oracle_dequant_bf16": (None, [_p, _p, _p, _p, _i, _i, _p]),
@@ -207,9 +207,10 @@ def philox4x64_10(ctr, key) -> np.ndarray:
     return out
 
 
-def requantize_lora(q, s, g: int, lb, la, alpha: float, seed: int):
+def requantize_lora(q, s, g: int, lb, la, alpha: float, seed: int, nearest: bool = False):
     """q int8 [E, N, K] (or [N, K]), s [E, N]; lb bf16 bits [E, N, r], la [E, r, K] (or without E).
-    Returns (codes int8, scales fp32) of the LoRA-patched weights, re-quantised with random rounding."""
+    Returns (codes int8, scales fp32) of the LoRA-patched weights, re-quantised with random rounding, or with
+    nearest rounding when `nearest` (then `seed` is unused)."""
     q = _c(q, np.int8)
     squeeze = q.ndim == 2
     if squeeze:
@@ -220,7 +221,7 @@ def requantize_lora(q, s, g: int, lb, la, alpha: float, seed: int):
     qo = np.empty_like(q)
     so = np.empty((E, N), np.float32)
     _check(load().oracle_requantize_lora(_ptr(q), _ptr(s), E, N, K, g, _ptr(lb), _ptr(la), r, float(alpha),
-                                         int(seed), _ptr(qo), _ptr(so)), "requantize_lora")
+                                         int(seed), int(bool(nearest)), _ptr(qo), _ptr(so)), "requantize_lora")
     return (qo[0], so[0]) if squeeze else (qo, so)
 
 

@@ -53,6 +53,9 @@
  *    generator, see oracle_philox4x64_10): counter ((e N + n) K/4 + k/4, 0, 0, 0), key (seed, 0), word
  *    k % 4, top 24 bits times 2^-24.  Delta sums in ascending rank index from +0.0f, separate multiply and
  *    add, then times alpha.  The pages fix none of these details (pinned by the oracle-pin tests).
+ *    The loader's second mode, which re-quantises each patched layer ([XB] "Inputs that matter":
+ *    Dynamic), takes the same patched values and fresh scale with nearest rounding instead,
+ *    code = clamp(rint(V / scale), -127, 127): the weight quantiser applied to V.
  *  - W6A8 / W4A8 with an FP8 scale per group of 16 ([NF2] "How they were made"; oracle_quantize_g16,
  *    oracle_linear_g16): the same block rotation; symmetric integer codes, qmax = 31 (6 bits) or 7 (4 bits);
  *    FP8 = E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite 448),
@@ -334,7 +337,7 @@ void oracle_philox4x64_10(const uint64_t* ctr, const uint64_t* key, uint64_t* ou
  *   (the difference is exact in fp32), so integers stay put and the rounding is unbiased to 2^-24. 
  * Returns 0, or -1 on a bad group or K (K must be a multiple of g and of 4). */
 int oracle_requantize_lora(const int8_t* q, const float* s, int E, int N, int K, int g, const uint16_t* lb,
-                           const uint16_t* la, int rank, float alpha, uint64_t seed, int8_t* q_out,
+                           const uint16_t* la, int rank, float alpha, uint64_t seed, int nearest, int8_t* q_out,
                            float* s_out) {
     int k4 = log4_of(g);
     if (k4 < 0 || K % g || K % 4 || rank < 0) return -1;
@@ -373,8 +376,12 @@ int oracle_requantize_lora(const int8_t* q, const float* s, int E, int N, int K,
             float c = 0.0f;
             if (sc != 0.0f) {
                 float t = v[k] / sc;
-                float fl = floorf(t);
-                c = fl + (u < t - fl ? 1.0f : 0.0f);
+                if (nearest) {
+                    c = rintf(t);
+                } else {
+                    float fl = floorf(t);
+                    c = fl + (u < t - fl ? 1.0f : 0.0f);
+                }
                 if (c > 127.0f) c = 127.0f;
                 if (c < -127.0f) c = -127.0f;
             }

@@ -127,11 +127,12 @@ def test_stage_validation(L):
     assert L.convrot_gemm_w8a8_bf16(P, P, 4, 96, P, P, 8, None, P, None) == SHAPE  # K % 64
     assert L.convrot_gemm_w8a8_bf16(P, P, 0, 128, P, P, 8, None, P, None) == SHAPE
     assert L.convrot_gemm_w8a8_bf16(P, None, 4, 128, P, P, 8, None, P, None) == NULL
-    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, None, None, 4, 1.0, 1, 1, P, P, None) == NULL
-    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, -1, 1.0, 1, 1, P, P, None) == SHAPE
-    assert L.convrot_requantize_lora(P, P, 1, 8, 500, 64, P, P, 4, 1.0, 1, 1, P, P, None) == GROUP
-    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, 4, float("inf"), 1, 1, P, P, None) == SHAPE
-    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, 4, 1.0, 1, 2, P, P, None) == SHAPE  # layout
+    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, None, None, 4, 1.0, 1, 0, 1, P, P, None) == NULL
+    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, -1, 1.0, 1, 0, 1, P, P, None) == SHAPE
+    assert L.convrot_requantize_lora(P, P, 1, 8, 500, 64, P, P, 4, 1.0, 1, 0, 1, P, P, None) == GROUP
+    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, 4, float("inf"), 1, 0, 1, P, P, None) == SHAPE
+    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, 4, 1.0, 1, 0, 2, P, P, None) == SHAPE  # layout
+    assert L.convrot_requantize_lora(P, P, 1, 8, 512, 64, P, P, 4, 1.0, 1, 2, 1, P, P, None) == SHAPE  # rounding
     nb = L.moe_route_workspace_bytes(100, 8)
     assert nb >= 100 * 8 * 4
     assert L.moe_route_expert_choice(P, 0, 100, 8, 101, P, P, None, P, nb, None) == SHAPE

@@ -148,3 +148,10 @@ def test_lora_requant_full_size_down_weights():
     rq, rs = oracle.requantize_lora(q, s, g, lb, la, 0.5, 2024)
     assert np.array_equal(host(st).view(np.uint32), rs.view(np.uint32)), "scales"
     assert np.array_equal(untile_codes(host(qt), E, N, K, 8), rq), "codes"
+    say("lora requant, nearest rounding")
+    qn, sn = cr.convrot_requantize_lora(dev(q), dev(s), g, dev_bf16(lb), dev_bf16(la), 0.5, 0,
+                                        rounding=cr.ROUND_NEAREST)
+    torch.cuda.synchronize()
+    rqn, rsn = oracle.requantize_lora(q, s, g, lb, la, 0.5, 0, nearest=True)
+    assert np.array_equal(host(sn).view(np.uint32), rsn.view(np.uint32)), "nearest scales"
+    assert np.array_equal(untile_codes(host(qn), E, N, K, 8), rqn), "nearest codes"

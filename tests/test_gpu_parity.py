@@ -221,6 +221,13 @@ def test_lora_requant_bit_exact(E, N, K, g, rank, alpha):
     if rank:  # without a delta the quotients are (nearly always) whole numbers: nothing random to round
         q_o, _ = cr.convrot_requantize_lora(qd, sd, g, lbd, lad, alpha, 78, layout=cr.LAYOUT_ROWMAJOR)
         assert not np.array_equal(host(q_o), rq), "another seed draws other roundings"
+    # the re-quantising mode: nearest rounding of the same patched values
+    rqn, rsn = oracle.requantize_lora(q, s, g, lb, la, alpha, seed=77, nearest=True)
+    for layout in (cr.LAYOUT_ROWMAJOR, cr.LAYOUT_MFMA):
+        q_n, s_n = cr.convrot_requantize_lora(qd, sd, g, lbd, lad, alpha, 5, layout=layout, rounding=cr.ROUND_NEAREST)
+        got = host(q_n) if layout == cr.LAYOUT_ROWMAJOR else untile_codes(host(q_n), E, N, K, 8)
+        assert np.array_equal(got, rqn), f"nearest codes (layout {layout})"
+        assert np.array_equal(host(s_n).view(np.uint32), rsn.view(np.uint32)), "nearest scales"
 
 
 # ----------------------------------------------------------------------------------------------------------

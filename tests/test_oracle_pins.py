@@ -533,6 +533,48 @@ def test_lora_requant_rounding_is_unbiased_and_seeded(orc):
     assert np.array_equal(q3, q2) and not np.array_equal(q4, q2)
 
 
+def test_lora_requant_nearest_mode(orc):
+    """The re-quantising mode rounds to nearest: without a delta it keeps the codes; with one, every code is the
+    nearest integer to V / scale for an fp64 reference of the rotated patch (away from half-integers), whatever
+    the seed; and a quotient of code + 0.3 (+ 0.7) always rounds down (up) where random rounding moves ~30 %."""
+    rng = np.random.default_rng(6)
+    q, s = _quantised_rows(rng, 2, 8, 512, pow2_scales=True)
+    lb0 = synth.to_bf16_bits(rng.standard_normal((2, 8, 0)).astype(np.float32))
+    la0 = synth.to_bf16_bits(rng.standard_normal((2, 0, 512)).astype(np.float32))
+    q2, s2 = orc.requantize_lora(q, s, 64, lb0, la0, 1.0, seed=7, nearest=True)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+    E, N, K, r, g = 2, 6, 512, 8, 64
+    q, s = _quantised_rows(rng, E, N, K)
+    lb = synth.to_bf16_bits((rng.standard_normal((E, N, r)) * 0.05).astype(np.float32))
+    la = synth.to_bf16_bits((rng.standard_normal((E, r, K)) * 0.05).astype(np.float32))
+    qn, sn = orc.requantize_lora(q, s, g, lb, la, 0.5, seed=11, nearest=True)
+    qn2, sn2 = orc.requantize_lora(q, s, g, lb, la, 0.5, seed=12, nearest=True)
+    assert np.array_equal(qn, qn2) and np.array_equal(sn, sn2)
+    _, sr = orc.requantize_lora(q, s, g, lb, la, 0.5, seed=11)
+    assert np.array_equal(sn, sr)  # same patched values, same fresh scale
+    bf = synth.bf16_bits_to_f32
+    delta = 0.5 * np.einsum("enr,erk->enk", bf(lb).astype(np.float64), bf(la).astype(np.float64))
+    h = scipy.linalg.hadamard(g).astype(np.float64) / math.sqrt(g)
+    v = q.astype(np.float64) * s[..., None] + (delta.reshape(E, N, K // g, g) @ h.T).reshape(E, N, K)
+    t = v / sn[..., None].astype(np.float64)
+    away = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-3
+    assert np.array_equal(qn[away], np.clip(np.round(t[away]), -127, 127).astype(np.int8))
+    assert np.abs(qn.astype(np.float64) - t).max() <= 0.5 + 1e-3
+
+    E, N, K, g = 1, 512, 256, 256
+    q = rng.integers(-100, 100, (E, N, K)).astype(np.int8)
+    q[..., 1] = 127
+    s = np.ones((E, N), np.float32)
+    ones = synth.to_bf16_bits(np.ones((E, N, 1), np.float32))
+    for frac, want in ((0.3, 0), (0.7, 1)):
+        cb = synth.to_bf16_bits(np.array([frac / 16], np.float32))
+        la = np.tile(cb, (E, 1, K)).reshape(E, 1, K)
+        qn, _ = orc.requantize_lora(q, s, g, ones, la, 1.0, seed=21, nearest=True)
+        assert np.all(qn[..., 0].astype(int) - q[..., 0].astype(int) == want)
+        assert np.array_equal(qn[..., 1:], q[..., 1:])
+
+
 # ----------------------------------------------------------------------------------------------------------
 # W6A8 / W4A8: FP8 (E4M3) scale per group of 16 (NitroFusion2 page, "How they were made")
 # ----------------------------------------------------------------------------------------------------------

@@ -53,7 +53,7 @@ _SIGS = {
     "convrot_quantize_prerotated": (_i, [_p, _i64, _i, _i, _p, _p, _p]),
     "convrot_gemm_i8_i32": (_i, [_p, _p, _i, _i, _i, _p, _p]),
     "convrot_gemm_w8a8_bf16": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _p]),
-    "convrot_requantize_lora": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _i, ctypes.c_float, ctypes.c_uint64, _i, _p, _p,
+    "convrot_requantize_lora": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _i, ctypes.c_float, ctypes.c_uint64, _i, _i, _p, _p,
                                      _p]),
     "moe_route_workspace_bytes": (_sz, [_i, _i]),
     "moe_route_expert_choice": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
@@ -282,10 +282,14 @@ def convrot_quantize_prerotated(r, bits: int = 8, q_out=None, s_out=None, stream
     return q_out, s_out
 
 
+ROUND_RANDOM, ROUND_NEAREST = 0, 1
+
+
 def convrot_requantize_lora(q, s, group: int, lora_b, lora_a, alpha: float, seed: int, layout: int = LAYOUT_MFMA,
-                            q_out=None, s_out=None, stream=None):
+                            q_out=None, s_out=None, stream=None, rounding: int = ROUND_RANDOM):
     """q int8 [E, N, K] (or [N, K]) row-major codes, s [E, N]; lora_b bf16 [E, N, r], lora_a bf16 [E, r, K]
-    (r = 0: both may be None).  Returns (codes in `layout`, scales fp32 [.., N])."""
+    (r = 0: both may be None).  rounding: ROUND_RANDOM (stochastic mode) or ROUND_NEAREST (re-quantising
+    mode).  Returns (codes in `layout`, scales fp32 [.., N])."""
     shape = q.shape
     E, N, K = (1, *shape) if q.dim() == 2 else shape
     r = 0 if lora_b is None else lora_b.shape[-1]
@@ -297,7 +301,7 @@ def convrot_requantize_lora(q, s, group: int, lora_b, lora_a, alpha: float, seed
     if s_out is None:
         s_out = _empty(shape[:-1], torch.float32, q)
     _check("convrot_requantize_lora", lib().convrot_requantize_lora(
-        _ptr(q), _ptr(s), E, N, K, group, _ptr(lora_b), _ptr(lora_a), r, float(alpha), int(seed), layout,
+        _ptr(q), _ptr(s), E, N, K, group, _ptr(lora_b), _ptr(lora_a), r, float(alpha), int(seed), int(rounding), layout,
         _ptr(q_out), _ptr(s_out), _stream(stream)))
     return q_out, s_out
 

@@ -259,9 +259,10 @@ convrot_status convrot_quantize_weights(const uint16_t* w, int E, int N, int K, 
 
 convrot_status convrot_requantize_lora(const int8_t* q_in, const float* s_in, int E, int N, int K, int group,
                                        const uint16_t* lora_b, const uint16_t* lora_a, int rank, float alpha,
-                                       uint64_t seed, int layout, int8_t* q_out, float* s_out,
+                                       uint64_t seed, int rounding, int layout, int8_t* q_out, float* s_out,
                                        hipStream_t stream) {
     if (!q_in || !s_in || !q_out || !s_out) return CONVROT_ERR_NULL;
+    if (rounding != CONVROT_ROUND_RANDOM && rounding != CONVROT_ROUND_NEAREST) return CONVROT_ERR_SHAPE;
     if (rank < 0 || rank > 4096) return CONVROT_ERR_SHAPE;
     if (rank > 0 && (!lora_b || !lora_a)) return CONVROT_ERR_NULL;
     if (layout != CONVROT_LAYOUT_ROWMAJOR && layout != CONVROT_LAYOUT_MFMA) return CONVROT_ERR_SHAPE;
@@ -273,7 +274,8 @@ convrot_status convrot_requantize_lora(const int8_t* q_in, const float* s_in, in
         (rank > 0 && (reinterpret_cast<uintptr_t>(lora_b) & 1)))
         return CONVROT_ERR_ALIGN;
     return hip_status(crk::launch_requantize_lora(q_in, s_in, E, N, K, group, lora_b, lora_a, rank, alpha, seed,
-                                                  layout == CONVROT_LAYOUT_MFMA, q_out, s_out, stream));
+                                                  rounding == CONVROT_ROUND_NEAREST, layout == CONVROT_LAYOUT_MFMA,
+                                                  q_out, s_out, stream));
 }
 
 size_t convrot_linear_workspace_bytes(int M, int K) {

@@ -12,10 +12,11 @@ namespace crk {
 hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, int8_t* q, float* s, float* rot,
                            hipStream_t st);
 // Weights [E, N, K]: row-major codes, or the MFMA-tiled layout when `tiled` (rows padded to blocks of 32).
-// LoRA patch of row-major int8 weights [E, N, K], re-quantised with random rounding (int8, row-major or tiled)
+// LoRA patch of row-major int8 weights [E, N, K], re-quantised with random or nearest rounding (int8,
+// row-major or tiled)
 hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, int N, int K, int group,
                                   const uint16_t* lb, const uint16_t* la, int rank, float alpha, uint64_t seed,
-                                  bool tiled, int8_t* qout, float* sout, hipStream_t st);
+                                  bool nearest, bool tiled, int8_t* qout, float* sout, hipStream_t st);
 // W6A8 / W4A8 with E4M3 group-16 scales: converter (row-major packing) and GEMM + dequant
 hipError_t launch_quantize_g16(const uint16_t* w, int N, int K, int group, int bits, uint8_t* q, uint8_t* f8,
                                float* s_row, hipStream_t st);

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void lora_requant_kernel(const int8_t* __restr
                                                            int64_t rows, int K, int N,
                                                            const uint16_t* __restrict__ lb,
                                                            const uint16_t* __restrict__ la, int rank, float alpha,
-                                                           uint64_t seed, int8_t* __restrict__ qout,
+                                                           uint64_t seed, int nearest, int8_t* __restrict__ qout,
                                                            float* __restrict__ sout) {
     constexpr bool kTiled = OUT == Out::kTiledI8;
     const int lane = threadIdx.x & 63;
@@ -352,8 +352,16 @@ __global__ __launch_bounds__(256) void lora_requant_kernel(const int8_t* __restr
         const int i = lane + 64 * j;
         if (i >= nvec) continue;
         int c[8];
+        if (nearest) {  // wave-uniform: the re-quantising mode, the weight quantiser on the patched values
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+            for (int e = 0; e < 8; ++e) {
+                float code = 0.0f;
+                if (scale != 0.0f) code = fminf(fmaxf(rintf(d[j].v[e] / scale), -127.0f), 127.0f);
+                c[e] = pad ? 0 : (int)code;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2 && !nearest; ++h) {
             uint64_t ctr[4] = {(uint64_t)(flat0 + 2 * i + h), 0, 0, 0};
             philox4x64_10(ctr, seed, 0);
 #pragma unroll
@@ -440,7 +448,7 @@ hipError_t launch_rotq_act(const uint16_t* x, int64_t rows, int K, int group, in
 
 hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, int N, int K, int group,
                                   const uint16_t* lb, const uint16_t* la, int rank, float alpha, uint64_t seed,
-                                  bool tiled, int8_t* qout, float* sout, hipStream_t st) {
+                                  bool nearest, bool tiled, int8_t* qout, float* sout, hipStream_t st) {
     const int64_t rows = (int64_t)E * N;
     if (rows == 0) return hipSuccess;
     const int nv = (K / 8 + 63) / 64;
@@ -450,10 +458,12 @@ hipError_t launch_requantize_lora(const int8_t* qin, const float* sin, int E, in
     if (group == GG && nv <= NVC) {                                                                           \
         if (tiled)                                                                                            \
             lora_requant_kernel<GG, NVC, Out::kTiledI8><<<grid, block, 0, st>>>(qin, sin, rows, K, N, lb, la, \
-                                                                                 rank, alpha, seed, qout, sout);\
+                                                                                 rank, alpha, seed, nearest,    \
+                                                                                 qout, sout);                   \
         else                                                                                                  \
             lora_requant_kernel<GG, NVC, Out::kRowI8><<<grid, block, 0, st>>>(qin, sin, rows, K, N, lb, la,   \
-                                                                               rank, alpha, seed, qout, sout);  \
+                                                                               rank, alpha, seed, nearest,      \
+                                                                               qout, sout);                     \
         return hipGetLastError();                                                                             \
     }
     CRK_LR(256, 4)
