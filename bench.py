@@ -421,6 +421,11 @@ def main():
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip the achievable-rate probes (int8 MFMA, HBM read) reported beside the roofline")
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="single-layer workloads: steps timed one by one after a 1 GiB scratch write (0 skips)")
+    ap.add_argument("--stack-layers", type=int, default=29,
+                    help="config 3: also time the weight-streaming stack of this many layers with 8- and 4-bit "
+                         "weights (0 skips)")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -432,6 +437,60 @@ def main():
     if args.workload == "g16":
         return run_g16(args)
 
+    return run_moe(args)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_launches(fn, iters, stream, warm=3):
+    """Mean duration in microseconds of `iters` back-to-back calls of fn (HIP events on `stream`)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    k0, k1 = _events(2)
+    k0.record(stream)
+    for _ in range(iters):
+        fn()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    return k0.elapsed_time(k1) / iters * 1e3
+
+
+def stack_sweep(cr, synth, s, n_layers, wbits, stream, dev, warm=2, sweeps=5):
+    """The weight-streaming regime: n_layers layers of the T-token shape, each with its own seeded weights and
+    logits drawn on the GPU, the same tokens; one sweep runs every layer once.  Returns (us per layer,
+    gate/up launch us with successive layers' weights)."""
+    import torch
+    layers = []
+    for li in range(n_layers):
+        lgd, w_gu_d, w_dn_d = synth.stack_layer_device(li, s, dev)
+        layers.append((lgd, cr.quantize_moe_weights(w_gu_d, w_dn_d, s.g_gu, s.g_dn, wbits)))
+        del w_gu_d, w_dn_d
+    x = torch.from_numpy(synth.stack_x(s).view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((s.T, s.d), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((s.E, s.C), dtype=torch.int32, device=dev)
+    wt = torch.empty((s.E, s.C), dtype=torch.float32, device=dev)
+    ws = torch.empty(cr.moe_expert_choice_workspace_bytes(s.T, s.C, layers[0][1]), dtype=torch.uint8, device=dev)
+
+    def sweep():
+        for lgd, w in layers:
+            cr.moe_expert_choice_forward(x, lgd, s.C, w, out=out, idx_out=idx, wt_out=wt, ws=ws, stream=stream)
+
+    us_sweep = time_launches(sweep, sweeps, stream, warm=warm)
+    qx, sx, _ = cr.convrot_rotq_rows(x, s.g_gu)
+    a = torch.empty((s.E * s.C, s.I), dtype=torch.bfloat16, device=dev)
+    it = iter(range(1 << 30))
+    gu_us = time_launches(lambda: cr.moe_gateup_swiglu(qx, sx, idx, layers[next(it) % n_layers][1], a_out=a,
+                                                       stream=stream), 2 * n_layers, stream)
+    del layers, ws
+    torch.cuda.empty_cache()
+    return us_sweep / n_layers, gu_us
+
+
+def run_moe(args):
     import torch
     from w8a8_rotated_int8_amd import binding as cr
     from w8a8_rotated_int8_amd import synth
@@ -482,7 +541,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = _events(2)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -499,20 +558,21 @@ def main():
     # launches take successive layers' weights, so each launch streams weights the previous ones did not touch.
     qx, sx, _ = cr.convrot_rotq_rows(xd, s.g_gu)
     a = torch.empty((s.E * s.C, s.I), dtype=torch.bfloat16, device=dev)
-    for i in range(3):
-        cr.moe_gateup_swiglu(qx, sx, idx, layers[i % n_layers][1], a_out=a, stream=stream)
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for i in range(args.kernel_iters):
-        cr.moe_gateup_swiglu(qx, sx, idx, layers[i % n_layers][1], a_out=a, stream=stream)
-    k1.record(stream)
-    torch.cuda.synchronize()
-    k_us = k0.elapsed_time(k1) / args.kernel_iters * 1e3
+    it = iter(range(1 << 30))
+    k_us = time_launches(lambda: cr.moe_gateup_swiglu(qx, sx, idx, layers[next(it) % n_layers][1], a_out=a,
+                                                      stream=stream), args.kernel_iters, stream)
+    # the down GEMM on the hidden rows of that launch, for the GEMM-only MFMA fraction
+    qa, sa, _ = cr.convrot_rotq_rows(a, s.g_dn)
+    z = torch.empty((s.E * s.C, s.d), dtype=torch.bfloat16, device=dev)
+    it = iter(range(1 << 30))
+    dn_us = time_launches(lambda: cr.moe_down_proj(qa, sa, s.C, layers[next(it) % n_layers][1], z_out=z,
+                                                   stream=stream), args.kernel_iters, stream)
     gb = gateup_bytes(s, args.wbits)
     achieved = gb / (k_us * 1e-6) / 1e9
     gemm_tops = gateup_ops(s) / (k_us * 1e-6) / 1e12
-    print(f"bench: gate/up GEMM {k_us:.1f} us/launch, {achieved:.0f} GB/s algorithmic, {gemm_tops:.0f} TOPS",
-          file=sys.stderr, flush=True)
+    gemm_only_tops = layer_ops(s) / ((k_us + dn_us) * 1e-6) / 1e12
+    print(f"bench: gate/up GEMM {k_us:.1f} us/launch, {achieved:.0f} GB/s algorithmic, {gemm_tops:.0f} TOPS; down "
+          f"GEMM {dn_us:.1f} us; both GEMMs {gemm_only_tops:.0f} TOPS", file=sys.stderr, flush=True)
 
     sec = ms * 1e-3 / n_layers  # one layer
     tops = layer_ops(s) / sec / 1e12
@@ -522,6 +582,7 @@ def main():
         workload = f"{n_layers} stacked {workload.replace('layer', 'layers', 1)}, each with its own weights and logits"
     # the committed counter summary covers the 8-bit gate/up launch at T=8192, C=256
     traffic = read_traffic() if (s.T, s.C, args.wbits) == (8192, 256, 8) else None
+    lbytes = layer_bytes(s, args.wbits)
     line = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -541,15 +602,54 @@ def main():
         "us_per_layer": round(sec * 1e6, 2),
         "tokens_per_s": round(s.T / sec, 1),
         "frac_int8_mfma_peak": round(tops / PEAK_INT8_TOPS, 4),
-        "frac_hbm_peak": round(layer_bytes(s, args.wbits) / sec / 1e9 / PEAK_HBM_GBS, 4),
+        "frac_hbm_peak": round(lbytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+        "gemm_only": {"gateup_us": round(k_us, 2), "down_us": round(dn_us, 2), "tops": round(gemm_only_tops, 1),
+                      "frac_int8_mfma_peak": round(gemm_only_tops / PEAK_INT8_TOPS, 4)},
         "roofline": {"kernel": "grouped gate/up INT8 GEMM + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "launch_us": round(k_us, 2),
                      "mfma_frac": round(gemm_tops / PEAK_INT8_TOPS, 4)},
         "cpu_baseline": None,
     }
+    if n_layers == 1 and args.cold_steps > 0:
+        # cold: a 1 GiB write between steps evicts the 256 MB memory-side cache and the L2s; each step is timed
+        # by its own event pair
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 255)
+            e0, e1 = _events(2)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        del scratch
+        cu = float(np.median(cold))
+        line["cold"] = {"us_per_layer": round(cu, 2), "tops": round(layer_ops(s) / (cu * 1e-6) / 1e12, 2),
+                        "tokens_per_s": round(s.T / (cu * 1e-6), 1),
+                        "frac_hbm_peak": round(lbytes / (cu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "steps": args.cold_steps, "note": "median over steps, each after a 1 GiB scratch write"}
+        print(f"bench: cold {cu:.1f} us/layer (median of {args.cold_steps})", file=sys.stderr, flush=True)
+    if args.config == 3 and args.stack_layers > 0:
+        st4 = synth.CONFIGS[4]
+        line["stack"] = {"layers": args.stack_layers,
+                         "workload": f"{args.stack_layers} stacked T={st4.T} layers, each with its own weights "
+                                     "and logits (weights drawn on the GPU), a sweep timed as a whole"}
+        for wbits in (8, 4):
+            lu, gu = stack_sweep(cr, synth, st4, args.stack_layers, wbits, stream, dev)
+            sb = layer_bytes(st4, wbits)
+            line["stack"][f"w{wbits}a8"] = {
+                "us_per_layer": round(lu, 2), "tops": round(layer_ops(st4) / (lu * 1e-6) / 1e12, 2),
+                "frac_hbm_peak": round(sb / (lu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                "gateup_us": round(gu, 2),
+                "gateup_frac_hbm_peak": round(gateup_bytes(st4, wbits) / (gu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            print(f"bench: stack of {args.stack_layers} layers, {wbits}-bit weights: {lu:.1f} us/layer, gate/up "
+                  f"{gu:.1f} us", file=sys.stderr, flush=True)
     if args.peaks:
         add_measured_peaks(line, stream, mfma_tops=gemm_tops, hbm_gbs=achieved)
+        line["gemm_only"]["frac_of_measured_int8_mfma_random"] = round(
+            gemm_only_tops / line["measured_peaks"]["int8_mfma_random_tops"], 4)
     if args.cpu_experts > 0:
         print(f"bench: timing the CPU oracle on {args.cpu_experts} experts", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x, lg, w_gu, w_dn, s, args.cpu_experts)
