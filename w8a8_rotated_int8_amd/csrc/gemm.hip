@@ -51,8 +51,6 @@ namespace crk {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 64;          // K bytes per pipeline stage (two MFMA slices)
@@ -118,7 +116,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int x) {
 
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
 struct GemmCfg {
-    static constexpr int TM = BM / 64;                 // 32-row blocks per wavefront (BM/2 rows)
     static constexpr int NBT = (WBITS == 8) ? 16 : 8;  // 1 KiB weight tiles per stage
     static constexpr int NBW = NBT / 4;                // weight DMAs per loader wavefront per stage
     static constexpr int A_BYTES = BM * kBK;
@@ -145,7 +142,7 @@ struct GemmCfg {
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmProblem p, int tiles_m, int tiles_n) {
     using Cfg = GemmCfg<BM, SB, SA, EPI, WBITS, TILED>;
-    constexpr int TM = Cfg::TM, NBW = Cfg::NBW, NAW = Cfg::NAW;
+    constexpr int NBW = Cfg::NBW, NAW = Cfg::NAW;
     constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
     constexpr int HALF = BM / 2;
     constexpr bool kScales = EPI != Epi::kI32;
@@ -331,76 +328,91 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         }
     };
 
-    v16i acc[TM][2];
+    // ---- fragments and accumulators ----
+    // The wavefront's BM/2 token rows are MS blocks of 16, taken in two halves of MH blocks by the half steps.
+    // Weight fragment (q, s) is rows 16 s .. 16 s + 15 of weight block q (my_blk0 / my_blk1).
+    // v_mfma_i32_16x16x64_i8 takes the weights as its first operand and a 16-token block as its second; for
+    // both, lane l holds row l % 16 and the 16 consecutive k of chunk l / 16 of the 64-deep step (the int32 sum
+    // is exact, so only the pairing of the two operands' bytes matters), and register i of the result is the
+    // product of weight row 4 (l / 16) + i with token l % 16.
+    constexpr int MS = BM / 32;
+    constexpr int MH = MS / 2;
+    static_assert(MH >= 1, "half steps need two token blocks per wavefront");
+    const int g4 = lane >> 4;  // the lane's k chunk; in the result, its 4-column group of each 16-column block
+    // per-lane byte offsets inside a stage: weight fragment (q, s) of block blk is at b_lane + (2 blk) KiB
+    // (int8: two 1 KiB tiles per 64 k, the chunk's tile g4 / 2) or b_lane + blk KiB (int4: one tile, 8-byte
+    // half g4 / 2), + 256 s; token block m at a_lane + (m * 16 + the half's first row) * 64 (swizzled chunks)
+    const int b_lane = (WBITS == 8) ? ((lane & 15) + 32 * (g4 & 1)) * 16 + 1024 * (g4 >> 1)
+                                    : ((lane & 15) + 32 * (g4 & 1)) * 16 + 8 * (g4 >> 1);
+    const int a_lane = (lane & 15) * kBK + ((g4 ^ ((lane >> 2) & 3)) << 4);
+
+    v4i acc[MS][2][2];
     auto clear_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int m = 0; m < MS; ++m)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][q][r] = 0;
+                for (int s = 0; s < 2; ++s) acc[m][q][s] = v4i{0, 0, 0, 0};
     };
-
-    // Fragments of one 32-deep slice s of the stage in ring slots (as, bs): this wavefront's two weight blocks
-    // and its TM activation row blocks.
-    auto read_slice = [&](int as, int bs, int s, v4i (&bf)[2], v4i (&af)[TM]) {
-        const int8_t* As = a_ring + as * A_BYTES;
-        const int8_t* Bs = b_ring + bs * B_BYTES + lane * 16;
+    auto read_b = [&](int bs, int q, int s) -> v4i {
+        const int blk = q ? my_blk1 : my_blk0;
+        const int8_t* p = b_ring + bs * B_BYTES + b_lane + 256 * s;
+        if constexpr (WBITS == 8) {
+            return *reinterpret_cast<const v4i*>(p + 2048 * blk);
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(p + 1024 * blk);
+            const uint2 u0 = unpack_nibbles(w.x), u1 = unpack_nibbles(w.y);
+            return v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
+        }
+    };
+    auto read_a = [&](int as, int m) -> v4i {
+        return *reinterpret_cast<const v4i*>(a_ring + as * A_BYTES + a_lane + (mh * HALF + 16 * m) * kBK);
+    };
+    // MFMAs of weight fragments bq[0..1] (block q) against the MH token blocks af, accumulating into blocks m0..
+    auto mfma_q = [&](int m0, int q, const v4i (&bq)[2], const v4i (&af)[MH]) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int blk = q ? my_blk1 : my_blk0;
-            if constexpr (WBITS == 8) {
-                bf[q] = *reinterpret_cast<const v4i*>(Bs + (2 * blk + s) * 1024);
-            } else {
-                const uint2 w = *reinterpret_cast<const uint2*>(Bs + blk * 1024 + 8 * s);
-                const uint2 u0 = unpack_nibbles(w.x), u1 = unpack_nibbles(w.y);
-                bf[q] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int m = 0; m < MH; ++m)
+                acc[m0 + m][q][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bq[s], af[m], acc[m0 + m][q][s], 0, 0, 0);
+    };
+    // n MFMAs alternating with r fragment reads, spread evenly
+    auto interleave = [&](auto nm_c, auto nr_c) {
+        constexpr int nm = decltype(nm_c)::value, nr = decltype(nr_c)::value;
+        if constexpr (nr == 0) {
+            __builtin_amdgcn_sched_group_barrier(0x008, nm, 0);
+        } else {
+            constexpr int per = nm / nr;
+#pragma unroll
+            for (int k = 0; k < nr; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
             }
+            if constexpr (nm > per * nr) __builtin_amdgcn_sched_group_barrier(0x008, nm - per * nr, 0);
         }
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-            af[tm] = *reinterpret_cast<const v4i*>(As + swz_offset(mh * HALF + tm * 32 + (lane & 31), 2 * s + (lane >> 5)));
-    };
-    auto mfma_slice = [&](const v4i (&bf)[2], const v4i (&af)[TM]) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                acc[tm][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[q], af[tm], acc[tm][q], 0, 0, 0);
-    };
-    // Scheduling of a half step: the 2 * TM MFMAs of one slice alternate with the 2 + TM fragment reads of the
-    // next slice, so the matrix pipe is fed while the LDS delivers.
-    auto interleave = [&]() {
-        constexpr int kMfma = 2 * TM, kReads = 2 + TM, kPairs = kMfma < kReads ? kMfma : kReads;
-#pragma unroll
-        for (int k = 0; k < kPairs; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
-        if constexpr (kMfma > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
-        if constexpr (kReads > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairs, 0);
     };
 
-    // Epilogue of tile i.  The weights are the MFMA's first operand, so lane l holds activation row l % 32 of
-    // each 32 x 32 block and, in register 4 j + i, weight row (output column) 8 j + 4 (l / 32) + i: each lane
-    // owns runs of 4 consecutive output columns, and the gate and up values of one output sit in the same lane.
+    // Epilogue of tile i.  Lane l holds, for token l % 16 of each 16-token block and each 16-column sub-block s
+    // of its weight blocks, the 4 consecutive output columns 16 s + 4 g4 .. + 3; the gate and up values of one
+    // output sit in the same lane and register.
     auto epilogue = [&](int i) {
         int e, nt, mt;
         decode(i, e, nt, mt);
-        const int h = lane >> 5;
         if constexpr (EPI == Epi::kI32) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int m = mt * BM + mh * HALF + tm * 32 + (lane & 31);
-                if (m >= M) continue;
+            for (int m = 0; m < MS; ++m) {
+                const int row = mt * BM + mh * HALF + 16 * m + (lane & 15);
+                if (row >= M) continue;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (n < N) static_cast<int32_t*>(p.out)[((int64_t)e * M + m) * N + n] = acc[tm][q][r];
-                    }
-                }
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int n = wblk(q ? my_blk1 : my_blk0, nt) * 32 + 16 * s + 4 * g4 + r;
+                            if (n < N) static_cast<int32_t*>(p.out)[((int64_t)e * M + row) * N + n] = acc[m][q][s][r];
+                        }
             }
         } else {
             const float* srow = srow_lds + (i % Cfg::NSC) * BM + mh * HALF;
@@ -409,72 +421,50 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
             const int rows_valid = (M - mt * BM) < BM ? (M - mt * BM) : BM;
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                 static_cast<uint16_t*>(p.out) + ((int64_t)e * M + mt * BM) * ldo, 0, rows_valid * ldo * 2, kBufferFlags);
-            // column scales (and bias) of weight block q of this wavefront, per run j: 4 consecutive columns
-            auto load_cs = [&](int q, float (&c)[16]) {
+            // column scales of weight block q for this lane: [s][r] = column 16 s + 4 g4 + r
+            auto load_cs = [&](int q, float (&c)[2][4]) {
                 const int blk = q ? my_blk1 : my_blk0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4i c4 = *reinterpret_cast<const v4i*>(csc + blk * 32 + 8 * j + 4 * h);
+                for (int s = 0; s < 2; ++s) {
+                    const v4i c4 = *reinterpret_cast<const v4i*>(csc + blk * 32 + 16 * s + 4 * g4);
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) c[4 * j + x] = __int_as_float(c4[x]);
+                    for (int r = 0; r < 4; ++r) c[s][r] = __int_as_float(c4[r]);
                 }
             };
-            auto load_bias = [&](int q, float (&b)[16]) {
-                const int blk = q ? my_blk1 : my_blk0;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int n = wblk(blk, nt) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    n = n < N ? n : N - 1;
-                    b[r] = bf16_to_float(p.bias[n]);
-                }
-            };
-            // One 32 x 32 output block: v[j][x] is this lane's row row0 + l % 32, column colb + 8 j + 4 (l / 32) + x.
-            // Packed to bf16, one swap between the lane halves per pair of runs gives lane l < 32 8-column chunk
-            // j0 of row l and lane l + 32 chunk j1 of the same row (A: chunks 0, 1; B: chunks 2, 3).  One swap
-            // between 16-lane rows then regroups A and B into X (rows 0-15) and Y (rows 16-31), where the four
-            // lanes l % 16 + {0, 16, 32, 48} hold chunks {0, 2, 1, 3} of row l % 16: each 16-byte store writes
-            // 64 contiguous bytes of 16 rows, half the write requests of 32-byte pieces.  Rows that are not
-            // 8-aligned fall back to element stores.  Every store is issued; out-of-range ones are dropped by
-            // the buffer range.
+            // One 16-token x 32-column output block: X (sub-block 0) and Y (sub-block 1) hold this lane's 4
+            // columns packed to bf16 (2 words each).  A swap between the lane halves gives lane groups 0-3 the
+            // values of groups (0, 1 | of X), (0, 1 | of Y) and (2, 3 | of X), (2, 3 | of Y); a swap between
+            // 16-lane rows then leaves group c with columns 8 c .. 8 c + 7, so each 16-byte buffer store writes
+            // 64 contiguous bytes of 16 rows.  Rows that are not 8-aligned fall back to element stores.  Every
+            // store is issued; out-of-range ones are dropped by the buffer range.
             const bool vec = (ldo & 7) == 0;
-            // pk[j][k]: columns 8 j + 4 (l / 32) + 2 k and + 1, packed to bf16
-            auto store_block = [&](int row0, int colb, const uint32_t (&pk)[4][2]) {
+            auto store_block = [&](int row0, int colb, const uint32_t (&X)[2], const uint32_t (&Y)[2]) {
+                const int r = row0 + (lane & 15);
                 if (vec) {
-                    const auto a0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
-                    const auto a1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
-                    const auto b0 = __builtin_amdgcn_permlane32_swap(pk[2][0], pk[3][0], false, false);
-                    const auto b1 = __builtin_amdgcn_permlane32_swap(pk[2][1], pk[3][1], false, false);
-                    const uint32_t A[4] = {a0[0], a1[0], a0[1], a1[1]};
-                    const uint32_t B[4] = {b0[0], b1[0], b0[1], b1[1]};
-                    uint32_t X[4], Y[4];
+                    uint32_t R[2], S[2];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const auto u = __builtin_amdgcn_permlane16_swap(A[k], B[k], false, false);
-                        X[k] = u[0];
-                        Y[k] = u[1];
+                    for (int d = 0; d < 2; ++d) {
+                        const auto u = __builtin_amdgcn_permlane32_swap(X[d], Y[d], false, false);
+                        const auto v = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
+                        R[d] = v[0];
+                        S[d] = v[1];
                     }
-                    const int col = colb + 8 * (((lane >> 4) & 1) * 2 + ((lane >> 5) & 1));  // chunk {0, 2, 1, 3}
-                    const int r = row0 + (lane & 15);
-                    const int offx = col < ldo ? (r * ldo + col) * 2 : kOobOffset;
-                    const int offy = col < ldo ? ((r + 16) * ldo + col) * 2 : kOobOffset;
-                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)X[0], (int)X[1], (int)X[2], (int)X[3]}, orsrc, offx,
+                    const int col = colb + 8 * g4;
+                    const int off = col < ldo ? (r * ldo + col) * 2 : kOobOffset;
+                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)R[0], (int)R[1], (int)S[0], (int)S[1]}, orsrc, off,
                                                            0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)Y[0], (int)Y[1], (int)Y[2], (int)Y[3]}, orsrc, offy,
-                                                           0, 0);
-                    ops += 2;
+                    ops += 1;
                 } else {
-                    const int r = row0 + (lane & 31);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int col = colb + 8 * j + 4 * h;
+                    for (int s = 0; s < 2; ++s)
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            const int off = col + x < ldo ? (r * ldo + col + x) * 2 : kOobOffset;
-                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk[j][x >> 1] >> (16 * (x & 1))), orsrc, off,
-                                                                  0, 0);
+                            const int col = colb + 16 * s + 4 * g4 + x;
+                            const uint32_t w = s ? Y[x >> 1] : X[x >> 1];
+                            const int off = col < ldo ? (r * ldo + col) * 2 : kOobOffset;
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w >> (16 * (x & 1))), orsrc, off, 0, 0);
                         }
-                    }
-                    ops += 16;
+                    ops += 8;
                 }
             };
             if constexpr (EPI == Epi::kBf16) {
@@ -482,96 +472,113 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const int colb = wblk(q ? my_blk1 : my_blk0, nt) * 32;
-                    auto rows_out = [&](auto with_bias, const float (&bias)[16]) {
+                    auto rows_out = [&](auto with_bias, const float (&bias)[2][4]) {
 #pragma unroll
-                        for (int tm = 0; tm < TM; ++tm) {
-                            const float sx = srow[tm * 32 + (lane & 31)];
-                            // the block's column scales, read again for each row block: fewer live registers
-                            float cs[16];
+                        for (int m = 0; m < MS; ++m) {
+                            const float sx = srow[16 * m + (lane & 15)];
+                            // the block's column scales, read again for each token block: fewer live registers
+                            float cs[2][4];
                             load_cs(q, cs);
-                            uint32_t pk[4][2];
+                            uint32_t XY[2][2];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
+                            for (int s = 0; s < 2; ++s)
 #pragma unroll
                                 for (int k = 0; k < 2; ++k) {
                                     float t[2];
 #pragma unroll
                                     for (int y = 0; y < 2; ++y) {
-                                        const int r = 4 * j + 2 * k + y;
-                                        t[y] = (float)acc[tm][q][r];
+                                        const int r = 2 * k + y;
+                                        t[y] = (float)acc[m][q][s][r];
                                         t[y] = t[y] * sx;
-                                        t[y] = t[y] * cs[r];
-                                        if constexpr (decltype(with_bias)::value) t[y] = t[y] + bias[r];
+                                        t[y] = t[y] * cs[s][r];
+                                        if constexpr (decltype(with_bias)::value) t[y] = t[y] + bias[s][r];
                                     }
-                                    pk[j][k] = pack_bf16x2(t[0], t[1]);
+                                    XY[s][k] = pack_bf16x2(t[0], t[1]);
                                 }
-                            store_block(mh * HALF + tm * 32, colb, pk);
+                            store_block(mh * HALF + 16 * m, colb, XY[0], XY[1]);
                         }
                     };
                     if (p.bias) {  // uniform: one copy of the loop per case
-                        float bias[16];
-                        load_bias(q, bias);
+                        float bias[2][4];
+                        const int blk = q ? my_blk1 : my_blk0;
+#pragma unroll
+                        for (int s = 0; s < 2; ++s)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                int n = wblk(blk, nt) * 32 + 16 * s + 4 * g4 + r;
+                                n = n < N ? n : N - 1;
+                                bias[s][r] = bf16_to_float(p.bias[n]);
+                            }
                         rows_out(std::true_type{}, bias);
                     } else {
-                        float unused[16];
+                        float unused[2][4];
                         rows_out(std::false_type{}, unused);
                     }
                 }
             } else {
-                float cg[16], cu[16];
+                float cg[2][4], cu[2][4];
                 load_cs(0, cg);
                 load_cs(1, cu);
                 const int colb = wblk(my_blk0, nt) * 32;  // gate block index = output column block
+                // window entry 2 (m - kSiluLo) + sign holds the gate with magnitude pattern m
+                const float* const silu_win = silu_lds - 2 * kSiluLo;
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const float sx = srow[tm * 32 + (lane & 31)];
+                for (int m = 0; m < MS; ++m) {
+                    const float sx = srow[16 * m + (lane & 15)];
                     // gate and up rounded to bf16 in one conversion; the gate's bits index the activation table
-                    uint32_t gu[16];
-                    float sg[16];
+                    uint32_t gu[2][4];
+                    float sg[2][4];
                     bool out_of_window = false;
-                    // window entry 2 (m - kSiluLo) + sign holds the gate with magnitude pattern m
-                    const float* const silu_win = silu_lds - 2 * kSiluLo;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float gt = (float)acc[tm][0][r];
-                        gt = gt * sx;
-                        gt = gt * cg[r];
-                        float up = (float)acc[tm][1][r];
-                        up = up * sx;
-                        up = up * cu[r];
-                        gu[r] = pack_bf16x2(gt, up);
-                        // magnitude pattern clamped into the window (one med3); a clamped value is out of it
-                        const uint32_t mag = gu[r] & 0x7fffu;
-                        const uint32_t mc = min(max(mag, kSiluLo), kSiluLo + kSiluSpan - 1u);
-                        out_of_window |= mag != mc;
-                        const uint32_t sgn = __builtin_amdgcn_ubfe(gu[r], 15, 1);
-                        sg[r] = silu_win[(mc << 1) + sgn];
-                    }
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float gt = (float)acc[m][0][s][r];
+                            gt = gt * sx;
+                            gt = gt * cg[s][r];
+                            float up = (float)acc[m][1][s][r];
+                            up = up * sx;
+                            up = up * cu[s][r];
+                            gu[s][r] = pack_bf16x2(gt, up);
+                            // magnitude pattern clamped into the window (one med3); a clamped value is out of it
+                            const uint32_t mag = gu[s][r] & 0x7fffu;
+                            const uint32_t mc = min(max(mag, kSiluLo), kSiluLo + kSiluSpan - 1u);
+                            out_of_window |= mag != mc;
+                            const uint32_t sgn = __builtin_amdgcn_ubfe(gu[s][r], 15, 1);
+                            sg[s][r] = silu_win[(mc << 1) + sgn];
+                        }
                     if (__builtin_expect(__ballot(out_of_window) != 0, 0)) {  // wave-uniform
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if ((gu[r] & 0x7fffu) - kSiluLo >= kSiluSpan) sg[r] = silu_fixed(__uint_as_float(gu[r] << 16));
-                    }
-                    uint32_t pk[4][2];
+                        for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                            for (int r = 0; r < 4; ++r)
+                                if ((gu[s][r] & 0x7fffu) - kSiluLo >= kSiluSpan)
+                                    sg[s][r] = silu_fixed(__uint_as_float(gu[s][r] << 16));
+                    }
+                    uint32_t XY[2][2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
 #pragma unroll
                         for (int k = 0; k < 2; ++k) {
-                            const int r = 4 * j + 2 * k;
-                            pk[j][k] = pack_bf16x2(sg[r] * __uint_as_float(gu[r] & 0xffff0000u),
-                                                   sg[r + 1] * __uint_as_float(gu[r + 1] & 0xffff0000u));
+                            const int r = 2 * k;
+                            XY[s][k] = pack_bf16x2(sg[s][r] * __uint_as_float(gu[s][r] & 0xffff0000u),
+                                                   sg[s][r + 1] * __uint_as_float(gu[s][r + 1] & 0xffff0000u));
                         }
-                    store_block(mh * HALF + tm * 32, colb, pk);
+                    store_block(mh * HALF + 16 * m, colb, XY[0], XY[1]);
                 }
             }
         }
     };
 
     // ---- the pipeline ----
-    // Stage g is consumed in two half steps.  Half step A: MFMAs of slice 0 while slice 1 is read from LDS.
-    // Then the wavefront waits for its own loads of stage g+1 and for its LDS reads, and the workgroup barrier
-    // publishes stage g+1 and frees the slots of stage g, which take the loads of stage g+S.  Half step B:
-    // MFMAs of slice 1 while slice 0 of stage g+1 is read.  Every ring keeps S stages in flight.
+    // Stage g is consumed in two half steps over the two halves of the wavefront's token blocks.  Half step A:
+    // the MFMAs of the first half while the second half's token fragments (and the block-1 weight fragments)
+    // are read from LDS.  Then the wavefront waits for its own loads of stage g+1 and for its LDS reads, and the
+    // workgroup barrier publishes stage g+1 and frees the slots of stage g, which take the loads of stage g+S.
+    // Half step B: the MFMAs of the second half while stage g+1's first-half token fragments are read, and,
+    // once the block-0 weight fragments are done, stage g+1's block-0 weight fragments into their registers
+    // (a scheduling barrier keeps those reads after the MFMAs that still use the old values).  Every ring keeps
+    // S stages in flight.
     int ld_i = 0, ld_kt = 0, ld_slot = 0, ld_left = total_stages;  // next stage to issue
     auto issue_next = [&]() {
         if (ld_left <= 0) return;
@@ -620,14 +627,22 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 #pragma unroll
     for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];  // hist[j]: end of stage g + 1 + j
 
-    v4i bf0[2], af0[TM], bf1[2], af1[TM];
+    v4i b0[2], b1[2], alo[MH], ahi[MH];
     int a_slot = 0, b_slot = 0, ci = 0, ckt = 0;
-    read_slice(0, 0, 0, bf0, af0);
+    b0[0] = read_b(0, 0, 0);
+    b0[1] = read_b(0, 0, 1);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) alo[m] = read_a(0, m);
     for (int g = 0; g + 1 < total_stages; ++g) {
-        // half step A: slice 0 of stage g with the reads of slice 1
-        read_slice(a_slot, b_slot, 1, bf1, af1);
-        mfma_slice(bf0, af0);
-        interleave();
+        // half step A: first token half of stage g, with the reads of its block-1 weights and second token half
+        b1[0] = read_b(b_slot, 1, 0);
+        b1[1] = read_b(b_slot, 1, 1);
+#pragma unroll
+        for (int m = 0; m < MH; ++m) ahi[m] = read_a(a_slot, MH + m);
+        mfma_q(0, 0, b0, alo);
+        mfma_q(0, 1, b1, alo);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        interleave(std::integral_constant<int, 4 * MH>{}, std::integral_constant<int, MH>{});
         wait_landed(ops - hist[0]);  // this wavefront's part of stage g + 1
         wait_lgkmcnt0();             // its reads of stage g (and any row-major ds_write)
         __builtin_amdgcn_s_barrier();
@@ -635,10 +650,17 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         a_slot = (a_slot + 1 == SA) ? 0 : a_slot + 1;
         b_slot = (b_slot + 1 == SB) ? 0 : b_slot + 1;
-        // half step B: slice 1 of stage g with the reads of slice 0 of stage g + 1
-        read_slice(a_slot, b_slot, 0, bf0, af0);
-        mfma_slice(bf1, af1);
-        interleave();
+        // half step B: second token half of stage g, with the reads of stage g + 1's first token half, then of
+        // its block-0 weights once the old ones are done
+#pragma unroll
+        for (int m = 0; m < MH; ++m) alo[m] = read_a(a_slot, m);
+        mfma_q(MH, 0, b0, ahi);
+        interleave(std::integral_constant<int, 2 * MH>{}, std::integral_constant<int, MH>{});
+        __builtin_amdgcn_sched_barrier(0);
+        b0[0] = read_b(b_slot, 0, 0);
+        b0[1] = read_b(b_slot, 0, 1);
+        mfma_q(MH, 1, b1, ahi);
+        interleave(std::integral_constant<int, 2 * MH>{}, std::integral_constant<int, 2>{});
 #pragma unroll
         for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];
         issue_next();  // stage g + S into the slots of stage g
@@ -654,9 +676,14 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         }
     }
     // last stage (always the last K-step of the last tile)
-    read_slice(a_slot, b_slot, 1, bf1, af1);
-    mfma_slice(bf0, af0);
-    mfma_slice(bf1, af1);
+    b1[0] = read_b(b_slot, 1, 0);
+    b1[1] = read_b(b_slot, 1, 1);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) ahi[m] = read_a(a_slot, MH + m);
+    mfma_q(0, 0, b0, alo);
+    mfma_q(0, 1, b1, alo);
+    mfma_q(MH, 0, b0, ahi);
+    mfma_q(MH, 1, b1, ahi);
     epilogue(ci);
 }
 
