@@ -42,6 +42,7 @@ struct Carver {
 struct MoeBuffers {
     float* probs_t;
     int32_t* slotmap;
+    uint64_t* tokmask;
     int8_t* qx;
     float* sx;
     int32_t* idx;
@@ -58,6 +59,7 @@ size_t plan_moe(void* ws, int T, int C, const convrot_moe_weights& w, MoeBuffers
     MoeBuffers m;
     m.probs_t = cv.take<float>((size_t)w.E * T);
     m.slotmap = cv.take<int32_t>((size_t)w.E * T);
+    m.tokmask = cv.take<uint64_t>((size_t)T * ((w.E + 63) / 64));
     m.qx = cv.take<int8_t>((size_t)T * w.d);
     m.sx = cv.take<float>((size_t)T);
     m.idx = cv.take<int32_t>(S);
@@ -170,19 +172,19 @@ convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_log
     const int64_t t1 = (int64_t)T * kRotqBesideSoftmaxPct / 100;
     const bool split = w.E <= 64 && crk::select_rotq_supported(T, w.E, w.d, w.group_gu);
     if (split) {
-        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, x, w.d, w.group_gu, b.qx, b.sx, t1,
-                                         stream));
-        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slotmap, x, w.d, w.group_gu, b.qx, b.sx,
-                                        t1, stream));
+        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, b.tokmask, x, w.d, w.group_gu, b.qx, b.sx,
+                                         t1, stream));
+        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, x, w.d, w.group_gu, b.qx,
+                                        b.sx, t1, stream));
     } else {
-        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, stream));
+        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, b.tokmask, stream));
         CRK_TRY(crk::launch_rotq_act(x, T, w.d, w.group_gu, b.qx, b.sx, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, stream));
+        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, stream));
     }
     CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, w, b.a), stream));
     CRK_TRY(crk::launch_rotq_act(b.a, S, w.I, w.group_dn, b.qa, b.sa, nullptr, stream));
     CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, w, b.z), stream));
-    CRK_TRY(crk::launch_combine(b.z, b.slotmap, wt, T, w.E, C, w.d, out, stream));
+    CRK_TRY(crk::launch_combine(b.z, b.slotmap, b.tokmask, wt, T, w.E, C, w.d, out, stream));
     return CONVROT_OK;
 }
 
@@ -470,8 +472,8 @@ convrot_status moe_route_expert_choice(const float* in, int is_probs, int T, int
     if (!ws || ws_bytes < moe_route_workspace_bytes(T, E)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
     float* probs_t = static_cast<float*>(ws);
-    CRK_TRY(crk::launch_softmax_t(in, is_probs ? 1 : 0, T, E, probs_t, probs_out, stream));
-    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, stream));
+    CRK_TRY(crk::launch_softmax_t(in, is_probs ? 1 : 0, T, E, probs_t, probs_out, nullptr, stream));
+    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, nullptr, stream));
     return CONVROT_OK;
 }
 
@@ -500,6 +502,7 @@ size_t moe_combine_workspace_bytes(int T, int E) {
     if (T < 1 || E < 1) return 0;
     Carver cv(nullptr);
     cv.take<int32_t>((size_t)E * T);
+    cv.take<uint64_t>((size_t)T * ((E + 63) / 64));
     return cv.used;
 }
 
@@ -512,9 +515,11 @@ convrot_status moe_combine(const uint16_t* z, const int32_t* idx, const float* w
     if (!aligned16(z) || !aligned16(idx) || !aligned16(wt) || !aligned16(out)) return CONVROT_ERR_ALIGN;
     if (!ws || ws_bytes < moe_combine_workspace_bytes(T, E)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
-    int32_t* slotmap = static_cast<int32_t*>(ws);
-    CRK_TRY(crk::launch_build_slotmap(idx, T, E, C, slotmap, stream));
-    CRK_TRY(crk::launch_combine(z, slotmap, wt, T, E, C, d, out, stream));
+    Carver cv(ws);
+    int32_t* slotmap = cv.take<int32_t>((size_t)E * T);
+    uint64_t* tokmask = cv.take<uint64_t>((size_t)T * ((E + 63) / 64));
+    CRK_TRY(crk::launch_build_slotmap(idx, T, E, C, slotmap, tokmask, stream));
+    CRK_TRY(crk::launch_combine(z, slotmap, tokmask, wt, T, E, C, d, out, stream));
     return CONVROT_OK;
 }
 

@@ -12,6 +12,9 @@
 //                tokens equal to it.  The list comes out in ascending token order without a sort; ties go
 //                to the lower token index by construction.
 //  build_slotmap per expert: slotmap[e, t] = position of t in expert e's list, or -1.
+//  Token masks: where asked for, bit e % 64 of word t * ceil(E / 64) + e / 64 is set when expert e takes token
+//  t (OR is order-independent, so the mask does not depend on which workgroup sets its bit first).  The softmax
+//  launch, which runs before the selection, clears the words of its tokens.
 #include "device_common.h"
 #include "kernels.h"
 #include "rotq_fast.h"
@@ -35,13 +38,15 @@ constexpr int kSmTrStride = kSmTok + 1;  // LDS row stride of the [expert][token
 
 // Tokens [32 b, 32 b + 32) (one 256-thread workgroup).
 __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int is_probs, int T, int E,
-                                             float* __restrict__ probs_t, float* __restrict__ probs_out, int b) {
+                                             float* __restrict__ probs_t, float* __restrict__ probs_out,
+                                             uint64_t* __restrict__ tokmask, int b) {
     __shared__ float tile[kSmTok * kSmStride];  // logits, then exponentials
     __shared__ float tr[64 * kSmTrStride];      // probabilities, transposed
     __shared__ float zrow[kSmTok];
     const int t0 = b * kSmTok;
     const int ntok = (T - t0) < kSmTok ? (T - t0) : kSmTok;
     const int tid = threadIdx.x, tok = tid >> 3, eg = tid & 7;
+    if (tokmask && tid < ntok) tokmask[t0 + tid] = 0ull;  // E <= 64: one mask word per token
     const float* src = in + (int64_t)t0 * E;
     const int n = ntok * E;  // the tile is contiguous in global memory
     if (E == 64 && ntok == kSmTok && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
@@ -121,8 +126,9 @@ __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int i
 }
 
 __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
-                                                              float* __restrict__ probs_t, float* __restrict__ probs_out) {
-    softmax_tile(in, is_probs, T, E, probs_t, probs_out, blockIdx.x);
+                                                              float* __restrict__ probs_t, float* __restrict__ probs_out,
+                                                              uint64_t* __restrict__ tokmask) {
+    softmax_tile(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x);
 }
 
 // The router softmax and token rotate+quantise in one launch: they do not depend on each other, so the first
@@ -130,12 +136,12 @@ __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __res
 // rotate+quantise workgroups fill the CUs the short softmax leaves idle, with no second stream to join.
 template <int G, int R>
 __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restrict__ logits, int T, int E,
-                                                           float* __restrict__ probs_t, int nsm,
-                                                           const uint16_t* __restrict__ x, int K,
+                                                           float* __restrict__ probs_t, uint64_t* __restrict__ tokmask,
+                                                           int nsm, const uint16_t* __restrict__ x, int K,
                                                            int8_t* __restrict__ qx, float* __restrict__ sx,
                                                            int64_t rows) {
     if ((int)blockIdx.x < nsm) {  // workgroup-uniform
-        softmax_tile(logits, 0, T, E, probs_t, nullptr, blockIdx.x);
+        softmax_tile(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x);
         return;
     }
     const int64_t row = (int64_t)(blockIdx.x - nsm) * 4 + (threadIdx.x >> 6);
@@ -145,9 +151,14 @@ __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restri
 
 // ---- softmax, any E (one thread per token) ------------------------------------------------------------
 __global__ __launch_bounds__(256) void softmax_t_kernel(const float* __restrict__ in, int is_probs, int T, int E,
-                                                        float* __restrict__ probs_t, float* __restrict__ probs_out) {
+                                                        float* __restrict__ probs_t, float* __restrict__ probs_out,
+                                                        uint64_t* __restrict__ tokmask) {
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= T) return;
+    if (tokmask) {
+        const int nw = (E + 63) >> 6;
+        for (int i = 0; i < nw; ++i) tokmask[(int64_t)t * nw + i] = 0ull;
+    }
     const float* l = in + (int64_t)t * E;
     if (is_probs) {
         for (int e = 0; e < E; ++e) {
@@ -247,7 +258,8 @@ __device__ __forceinline__ int lanes_below(int v, int& total) {
 template <int KR>
 __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ probs_t, int T, int C,
                                                     int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                    int32_t* __restrict__ slotmap, int e) {
+                                                    int32_t* __restrict__ slotmap, uint64_t* __restrict__ tokmask,
+                                                    int nw, int e) {
     __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
     __shared__ uint32_t s_red[2 * kSelV];
     __shared__ uint32_t s_bcast[2];
@@ -412,6 +424,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
             slot[c] = sel ? pos : -1;
             if (sel && pos < C) {
                 idx[(int64_t)e * C + pos] = t + c;
+                if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
                 float v_out;
                 if constexpr (kKeepVal) {
                     v_out = val[j][c];
@@ -441,8 +454,9 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
 template <int KR>
 __global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                    int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                   int32_t* __restrict__ slotmap) {
-    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, blockIdx.x);
+                                                                   int32_t* __restrict__ slotmap,
+                                                                   uint64_t* __restrict__ tokmask, int nw) {
+    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x);
 }
 
 // The selection and the rest of the token rotate+quantise in one launch: the first E workgroups select (one
@@ -451,11 +465,12 @@ template <int KR, int G, int R>
 __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __restrict__ probs_t, int T, int C, int E,
                                                                  int32_t* __restrict__ idx, float* __restrict__ wt,
                                                                  int32_t* __restrict__ slotmap,
+                                                                 uint64_t* __restrict__ tokmask, int nw,
                                                                  const uint16_t* __restrict__ x, int K,
                                                                  int8_t* __restrict__ qx, float* __restrict__ sx,
                                                                  int64_t row0) {
     if ((int)blockIdx.x < E) {  // workgroup-uniform
-        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, blockIdx.x);
+        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x);
         return;
     }
     const int64_t row = row0 + (int64_t)(blockIdx.x - E) * kSelV + (threadIdx.x >> 6);
@@ -466,7 +481,8 @@ __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __
 // Any T: keys re-read from global memory in each pass.
 __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                  int32_t* __restrict__ slotmap) {
+                                                                  int32_t* __restrict__ slotmap,
+                                                                  uint64_t* __restrict__ tokmask, int nw) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_prefix, s_remaining;
     __shared__ int scratch[kSelWaves];
@@ -539,6 +555,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* _
         if (sel && pos < C) {
             idx[(int64_t)e * C + pos] = t;
             wt[(int64_t)e * C + pos] = pv;
+            if (tokmask) atomicOr(tokmask + (int64_t)t * nw + (e >> 6), 1ull << (e & 63));
         }
         if (valid && slotmap) slotmap[(int64_t)e * T + t] = sel ? pos : -1;
         carry_eq += tot_eq;
@@ -547,31 +564,42 @@ __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* _
 }
 
 __global__ __launch_bounds__(1024) void build_slotmap_kernel(const int32_t* __restrict__ idx, int T, int C,
-                                                             int32_t* __restrict__ slotmap) {
+                                                             int32_t* __restrict__ slotmap,
+                                                             uint64_t* __restrict__ tokmask, int nw) {
     const int e = blockIdx.x;
     int32_t* row = slotmap + (int64_t)e * T;
     for (int t = threadIdx.x; t < T; t += 1024) row[t] = -1;
     __syncthreads();
     for (int c = threadIdx.x; c < C; c += 1024) {
         const int t = idx[(int64_t)e * C + c];
-        if (t >= 0 && t < T) row[t] = c;  // entries outside [0, T) are ignored
+        if (t >= 0 && t < T) {  // entries outside [0, T) are ignored
+            row[t] = c;
+            atomicOr(tokmask + (int64_t)t * nw + (e >> 6), 1ull << (e & 63));
+        }
     }
+}
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint64_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0ull;
 }
 
 }  // namespace
 
 hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* probs_t, float* probs_out,
-                            hipStream_t st) {
+                            uint64_t* tokmask, hipStream_t st) {
     if (E <= 64)
         softmax_t_small_kernel<<<dim3((T + kSmTok - 1) / kSmTok), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t,
-                                                                                      probs_out);
+                                                                                      probs_out, tokmask);
     else
-        softmax_t_kernel<<<dim3((T + 255) / 256), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t, probs_out);
+        softmax_t_kernel<<<dim3((T + 255) / 256), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t, probs_out,
+                                                                      tokmask);
     return hipGetLastError();
 }
 
-hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, const uint16_t* x, int K,
-                               int group, int8_t* qx, float* sx, int64_t rows, hipStream_t st) {
+hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, uint64_t* tokmask,
+                               const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t rows,
+                               hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (E > 64 || K % (8 * group) != 0 || rows < 0 || rows > T) return hipErrorNotSupported;
     const int nsm = (T + kSmTok - 1) / kSmTok;
@@ -580,7 +608,8 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
     const int R = K / (8 * group);
 #define CRK_SR(GG, RR)                                                                                  \
     if (group == GG && R == RR) {                                                                       \
-        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, nsm, x, K, qx, sx, rows); \
+        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, tokmask, nsm, x, K, qx, sx, \
+                                                            rows);                                            \
         return hipGetLastError();                                                                       \
     }
     CRK_SR(256, 1)
@@ -594,11 +623,13 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
 }
 
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
-                              int32_t* slotmap, hipStream_t st) {
-#define CRK_SEL(K)                                                                                      \
-    if (T <= kSelV * 256 * K) {                                                                         \
-        select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slotmap); \
-        return hipGetLastError();                                                                       \
+                              int32_t* slotmap, uint64_t* tokmask, hipStream_t st) {
+    const int nw = (E + 63) >> 6;
+#define CRK_SEL(K)                                                                                              \
+    if (T <= kSelV * 256 * K) {                                                                                 \
+        select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, \
+                                                                      nw);                                      \
+        return hipGetLastError();                                                                               \
     }
     CRK_SEL(1)
     CRK_SEL(2)
@@ -606,7 +637,7 @@ hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t
     CRK_SEL(8)
     CRK_SEL(16)
 #undef CRK_SEL
-    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap);
+    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, nw);
     return hipGetLastError();
 }
 
@@ -616,16 +647,17 @@ bool select_rotq_supported(int T, int E, int K, int group) {
 }
 
 hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
-                              const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t row0,
-                              hipStream_t st) {
+                              uint64_t* tokmask, const uint16_t* x, int K, int group, int8_t* qx, float* sx,
+                              int64_t row0, hipStream_t st) {
+    const int nw = (E + 63) >> 6;
     if (!select_rotq_supported(T, E, K, group) || row0 < 0 || row0 > T) return hipErrorNotSupported;
     const int R = K / (8 * group);
     const int64_t nrot = (T - row0 + kSelV - 1) / kSelV;
     const dim3 grid((unsigned)(E + nrot)), block(kSelV * 64);
 #define CRK_SR2(KK, GG, RR)                                                                                 \
     if (T <= kSelV * 256 * KK && group == GG && R == RR) {                                                  \
-        select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slotmap, x, K, qx, sx, \
-                                                               row0);                                      \
+        select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slotmap, tokmask, nw, \
+                                                               x, K, qx, sx, row0);                        \
         return hipGetLastError();                                                                           \
     }
 #define CRK_SR2_G(KK) CRK_SR2(KK, 256, 1) CRK_SR2(KK, 256, 2) CRK_SR2(KK, 256, 4) CRK_SR2(KK, 64, 1) \
@@ -639,8 +671,12 @@ hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t
     return hipErrorNotSupported;
 }
 
-hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, hipStream_t st) {
-    build_slotmap_kernel<<<dim3(E), dim3(1024), 0, st>>>(idx, T, C, slotmap);
+hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, uint64_t* tokmask,
+                                hipStream_t st) {
+    const int nw = (E + 63) >> 6;
+    const int64_t words = (int64_t)T * nw;
+    clear_words_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(tokmask, words);
+    build_slotmap_kernel<<<dim3(E), dim3(1024), 0, st>>>(idx, T, C, slotmap, tokmask, nw);
     return hipGetLastError();
 }
 
