@@ -1,4 +1,4 @@
-// Grouped INT8 x INT8 -> INT32 GEMM on gfx950 MFMA (v_mfma_i32_32x32x32_i8) with fused epilogues:
+// Grouped INT8 x INT8 -> INT32 GEMM on gfx950 MFMA (v_mfma_i32_16x16x64_i8) with fused epilogues:
 //   kI32    exact int32 accumulators (test export, plain GEMM)
 //   kBf16   bf16( ((float)acc * s_act[row]) * s_w[n] ) [+ bias]      (single linear, expert down proj)
 //   kSwiGLU gate and up of the same column in one wavefront, each dequantised to bf16, then
@@ -19,14 +19,13 @@
 // w % 4 (for SwiGLU the gate block and the up block of the same 32 output columns, so the epilogue pairs
 // them in registers).
 //
-// Main loop: K-steps of 64 bytes (two 32-deep MFMA slices), one pipeline running across all tiles of the
-// workgroup, so the loads of the next tile's first stages overlap the current tile's last steps and its
-// epilogue.
+// Main loop: K-steps of 64 bytes (one MFMA deep), one pipeline running across all tiles of the workgroup, so
+// the loads of the next tile's first stages overlap the current tile's last steps and its epilogue.
 //   * Every operand moves global -> LDS with gfx950's global_load_lds (no register staging): the weights, the
 //     gathered activation rows, the per-tile row indices, row scales and column scales.
-//   * Weights are stored MFMA-tiled: each (32-row block, K-block) tile is 1 KiB in B-operand lane order, so a
-//     DMA is one coalesced 16-byte load per lane (non-temporal: each byte is used once) and the fragment read
-//     is one ds_read_b128.  Activation rows are 64 bytes per stage with the 16-byte chunks XOR-swizzled by
+//   * Weights are stored MFMA-tiled: each (32-row block, K-block) tile is 1 KiB in lane order, so a DMA is one
+//     coalesced 16-byte load per lane (non-temporal: each byte is used once) and a fragment read is one
+//     ds_read_b128 (ds_read_b64 and an unpack for 4-bit weights).  Activation rows are 64 bytes per stage with the 16-byte chunks XOR-swizzled by
 //     (row / 4) % 4, so the fragment reads are free of bank conflicts.
 //   * Load roles: wavefronts 0-3 issue the weight DMAs into an SB-deep ring, wavefronts 4-7 the activation
 //     DMAs into an SA-deep ring.  A wavefront's vector memory operations complete in issue order, so waiting
@@ -35,10 +34,13 @@
 //     always issued and drop out-of-range lanes in hardware) and waits with that exact X, so each ring keeps
 //     its full depth in flight through tile boundaries and epilogues.  Operations left out of the count can
 //     only make a wait stricter.
-//   * Half steps: the MFMAs of a stage's first slice run while its second slice is read from LDS; then one
-//     workgroup barrier publishes the next stage (and frees the slots of this one for the loads S stages
-//     ahead), and the MFMAs of the second slice run while the first slice of the next stage is read.  The
-//     matrix pipe never waits for a whole stage of fragment reads.
+//   * Half steps: v_mfma_i32_16x16x64_i8 multiplies a 16-row weight fragment by a 16-token block over a whole
+//     64-deep stage.  The MFMAs of the first half of a wavefront's token blocks run while the second half's
+//     fragments are read from LDS; then one workgroup barrier publishes the next stage (and frees the slots of
+//     this one for the loads S stages ahead), and the MFMAs of the second half run while the next stage's first
+//     token half and all its weight fragments are read into a second set of registers.  The matrix pipe never
+//     waits for a whole stage of fragment reads, and no weight fragment (nor its 4-bit unpacking) is read just
+//     before its first use.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
 #include <atomic>
@@ -112,6 +114,15 @@ __device__ __forceinline__ void wait_vmcnt_range(int x) {
 __device__ __forceinline__ void wait_vmcnt_dyn(int x) {
     x = x < 0 ? 0 : (x > 63 ? 63 : x);  // a smaller count is a stricter wait
     wait_vmcnt_range<0, 63>(x);
+}
+
+// Scheduling of NM MFMAs with NR LDS fragment reads spread evenly among them (group K of NR).
+template <int NM, int NR, int K>
+__device__ __forceinline__ void spread_reads() {
+    constexpr int cnt = (K + 1) * NM / NR - K * NM / NR;
+    if constexpr (cnt > 0) __builtin_amdgcn_sched_group_barrier(0x008, cnt, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             // DS read
+    if constexpr (K + 1 < NR) spread_reads<NM, NR, K + 1>();
 }
 
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
@@ -377,19 +388,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
             for (int m = 0; m < MH; ++m)
                 acc[m0 + m][q][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bq[s], af[m], acc[m0 + m][q][s], 0, 0, 0);
     };
-    // n MFMAs alternating with r fragment reads, spread evenly
+    // nm MFMAs and nr fragment reads, the reads spread evenly among the MFMAs
     auto interleave = [&](auto nm_c, auto nr_c) {
         constexpr int nm = decltype(nm_c)::value, nr = decltype(nr_c)::value;
         if constexpr (nr == 0) {
             __builtin_amdgcn_sched_group_barrier(0x008, nm, 0);
         } else {
-            constexpr int per = nm / nr;
-#pragma unroll
-            for (int k = 0; k < nr; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-            }
-            if constexpr (nm > per * nr) __builtin_amdgcn_sched_group_barrier(0x008, nm - per * nr, 0);
+            spread_reads<nm, nr, 0>();
         }
     };
 
@@ -572,13 +577,11 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 
     // ---- the pipeline ----
     // Stage g is consumed in two half steps over the two halves of the wavefront's token blocks.  Half step A:
-    // the MFMAs of the first half while the second half's token fragments (and the block-1 weight fragments)
-    // are read from LDS.  Then the wavefront waits for its own loads of stage g+1 and for its LDS reads, and the
-    // workgroup barrier publishes stage g+1 and frees the slots of stage g, which take the loads of stage g+S.
-    // Half step B: the MFMAs of the second half while stage g+1's first-half token fragments are read, and,
-    // once the block-0 weight fragments are done, stage g+1's block-0 weight fragments into their registers
-    // (a scheduling barrier keeps those reads after the MFMAs that still use the old values).  Every ring keeps
-    // S stages in flight.
+    // the MFMAs of the first half while the second half's token fragments are read from LDS.  Then the
+    // wavefront waits for its own loads of stage g+1 and for its LDS reads, and the workgroup barrier publishes
+    // stage g+1 and frees the slots of stage g, which take the loads of stage g+S.  Half step B: the MFMAs of
+    // the second half while stage g+1's first-half token fragments and all its weight fragments are read.
+    // Every ring keeps S stages in flight.
     int ld_i = 0, ld_kt = 0, ld_slot = 0, ld_left = total_stages;  // next stage to issue
     auto issue_next = [&]() {
         if (ld_left <= 0) return;
@@ -627,21 +630,22 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 #pragma unroll
     for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];  // hist[j]: end of stage g + 1 + j
 
-    v4i b0[2], b1[2], alo[MH], ahi[MH];
+    // weight fragments of the current stage (bc) and of the next (bn), read during half step B
+    v4i bc0[2], bc1[2], bn0[2], bn1[2], alo[MH], ahi[MH];
     int a_slot = 0, b_slot = 0, ci = 0, ckt = 0;
-    b0[0] = read_b(0, 0, 0);
-    b0[1] = read_b(0, 0, 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bc0[s] = read_b(0, 0, s);
+        bc1[s] = read_b(0, 1, s);
+    }
 #pragma unroll
     for (int m = 0; m < MH; ++m) alo[m] = read_a(0, m);
     for (int g = 0; g + 1 < total_stages; ++g) {
-        // half step A: first token half of stage g, with the reads of its block-1 weights and second token half
-        b1[0] = read_b(b_slot, 1, 0);
-        b1[1] = read_b(b_slot, 1, 1);
+        // half step A: first token half of stage g, with the reads of its second token half
 #pragma unroll
         for (int m = 0; m < MH; ++m) ahi[m] = read_a(a_slot, MH + m);
-        mfma_q(0, 0, b0, alo);
-        mfma_q(0, 1, b1, alo);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        mfma_q(0, 0, bc0, alo);
+        mfma_q(0, 1, bc1, alo);
         interleave(std::integral_constant<int, 4 * MH>{}, std::integral_constant<int, MH>{});
         wait_landed(ops - hist[0]);  // this wavefront's part of stage g + 1
         wait_lgkmcnt0();             // its reads of stage g (and any row-major ds_write)
@@ -650,17 +654,22 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         a_slot = (a_slot + 1 == SA) ? 0 : a_slot + 1;
         b_slot = (b_slot + 1 == SB) ? 0 : b_slot + 1;
-        // half step B: second token half of stage g, with the reads of stage g + 1's first token half, then of
-        // its block-0 weights once the old ones are done
+        // half step B: second token half of stage g, with the reads of stage g + 1's first token half and weights
 #pragma unroll
         for (int m = 0; m < MH; ++m) alo[m] = read_a(a_slot, m);
-        mfma_q(MH, 0, b0, ahi);
-        interleave(std::integral_constant<int, 2 * MH>{}, std::integral_constant<int, MH>{});
-        __builtin_amdgcn_sched_barrier(0);
-        b0[0] = read_b(b_slot, 0, 0);
-        b0[1] = read_b(b_slot, 0, 1);
-        mfma_q(MH, 1, b1, ahi);
-        interleave(std::integral_constant<int, 2 * MH>{}, std::integral_constant<int, 2>{});
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bn0[s] = read_b(b_slot, 0, s);
+            bn1[s] = read_b(b_slot, 1, s);
+        }
+        mfma_q(MH, 0, bc0, ahi);
+        mfma_q(MH, 1, bc1, ahi);
+        interleave(std::integral_constant<int, 4 * MH>{}, std::integral_constant<int, MH + 4>{});
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bc0[s] = bn0[s];
+            bc1[s] = bn1[s];
+        }
 #pragma unroll
         for (int t = 0; t + 1 < Cfg::SMAX; ++t) hist[t] = hist[t + 1];
         issue_next();  // stage g + S into the slots of stage g
@@ -676,14 +685,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
         }
     }
     // last stage (always the last K-step of the last tile)
-    b1[0] = read_b(b_slot, 1, 0);
-    b1[1] = read_b(b_slot, 1, 1);
 #pragma unroll
     for (int m = 0; m < MH; ++m) ahi[m] = read_a(a_slot, MH + m);
-    mfma_q(0, 0, b0, alo);
-    mfma_q(0, 1, b1, alo);
-    mfma_q(MH, 0, b0, ahi);
-    mfma_q(MH, 1, b1, ahi);
+    mfma_q(0, 0, bc0, alo);
+    mfma_q(0, 1, bc1, alo);
+    mfma_q(MH, 0, bc0, ahi);
+    mfma_q(MH, 1, bc1, ahi);
     epilogue(ci);
 }
 
