@@ -10,6 +10,7 @@ operands, HBM read through LDS DMA) for ``bench.py``.
     python -m w8a8_rotated_int8_amd.profiling copy <MiB> <iters>
     python -m w8a8_rotated_int8_amd.profiling traffic <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir>
         <copy_MiB> <kernel_substring> <out.txt> "<commands>"
+    python -m w8a8_rotated_int8_amd.profiling pmc <out.txt> "<commands>" <label=kernel_substring>,... <run_dir>...
 """
 from __future__ import annotations
 
@@ -104,6 +105,71 @@ def counter_per_dispatch(run_dir: str, counter: str, pattern: str, skip: int = 1
     return sum(per[i] for i in ids) / len(ids), len(ids)
 
 
+N_XCD = 8          # GRBM_GUI_ACTIVE comes summed over the XCDs
+N_SIMD = 256 * 4   # MFMA units: 4 SIMDs in each of the 256 compute units
+
+
+def _dispatches(run_dir: str, pattern: str, skip: int = 1):
+    """{dispatch id: {counter: value summed over its dimensions}} and the durations in us, for the dispatches
+    whose kernel name contains `pattern` (the first `skip` dropped as warm-up)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = {}
+    for r in _csv(run_dir, "counter_collection"):
+        if pattern not in r["Kernel_Name"]:
+            continue
+        k = int(r["Dispatch_Id"])
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[k] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    ids = sorted(per)
+    if len(ids) > skip:
+        ids = ids[skip:]
+    return {k: per[k] for k in ids}, [dur[k] for k in ids]
+
+
+def pmc_summary(out_txt: str, command: str, kernels: str, run_dirs) -> None:
+    """Counters of the named kernels, one collection pass per run directory, averaged per dispatch, with the
+    derived figures: clock (GRBM_GUI_ACTIVE per XCD over the dispatch time), MFMA busy fraction (MFMA busy
+    cycles over all SIMDs' cycles), per-cycle rates of the SQ / TA / TD counters and the mean L2 read latency
+    seen by the vector caches."""
+    lines = [f"command: {command}", "source: rocprofv3 --pmc (counter_collection.csv), one pass per counter set;",
+             "  values are means per dispatch after the first; the profiler serialises dispatches, so the clock",
+             "  here is the unthrottled one", f"gemm_source_sha256_16: "
+             f"{hashlib.sha256(open(GEMM_SRC, 'rb').read()).hexdigest()[:16]}", ""]
+    for spec in kernels.split(","):
+        label, pattern = spec.split("=", 1)
+        lines.append(f"== {label} (kernel name contains {pattern!r})")
+        for d in run_dirs:
+            disp, durs = _dispatches(d, pattern)
+            if not disp:
+                lines.append(f"  pass {os.path.basename(d.rstrip('/'))}: no dispatch")
+                continue
+            names = sorted({c for v in disp.values() for c in v})
+            avg = {c: sum(v.get(c, 0.0) for v in disp.values()) / len(disp) for c in names}
+            us = sum(durs) / len(durs)
+            lines.append(f"  pass {os.path.basename(d.rstrip('/'))}: {len(disp)} dispatches, {us:.1f} us each")
+            grbm = avg.get("GRBM_GUI_ACTIVE", 0.0)
+            cyc = grbm / N_XCD
+            if cyc > 0:
+                lines.append(f"    clock: {cyc / us * 1e-3:.2f} GHz ({cyc:.4g} cycles per XCD)")
+            for c in names:
+                if c == "GRBM_GUI_ACTIVE":
+                    continue
+                rate = f"  ({avg[c] / cyc:.4g} per cycle)" if cyc > 0 else ""
+                lines.append(f"    {c}: {avg[c]:.4g}{rate}")
+            if cyc > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                lines.append(f"    MFMA busy: {100.0 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_SIMD):.1f} % "
+                             f"of {N_SIMD} SIMDs")
+            if avg.get("TCP_TCC_READ_REQ_sum", 0.0) > 0:
+                lines.append(f"    L2 read latency: {avg['TCP_TCC_READ_REQ_LATENCY_sum'] / avg['TCP_TCC_READ_REQ_sum']:.0f}"
+                             " cycles per request")
+            if avg.get("SQ_LDS_IDX_ACTIVE", 0.0) > avg.get("SQ_LDS_BANK_CONFLICT", 0.0) > 0:
+                lines.append(f"    LDS bank conflict ratio: {avg['SQ_LDS_BANK_CONFLICT'] / (avg['SQ_LDS_IDX_ACTIVE'] - avg['SQ_LDS_BANK_CONFLICT']):.3f}")
+        lines.append("")
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_probe(mib: int, iters: int) -> None:
     """Plain device-to-device copy of `mib` MiB, `iters` times (counter calibration)."""
     import torch
@@ -148,5 +214,7 @@ if __name__ == "__main__":
         copy_probe(int(sys.argv[2]), int(sys.argv[3]))
     elif cmd == "traffic":
         traffic_summary(*sys.argv[2:6], int(sys.argv[6]), sys.argv[7], sys.argv[8], sys.argv[9])
+    elif cmd == "pmc":
+        pmc_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     else:
         sys.exit(__doc__)
