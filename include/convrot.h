@@ -79,11 +79,12 @@ const char* convrot_status_str(convrot_status s);
  *  CONVROT_LAYOUT_ROWMAJOR: codes of row n, column k at byte n*K + k (int8), or nibble k%2 of byte
  *    n*(K/2) + k/2 (int4; even k in bits 0-3).  Interchange / inspection format.
  *  CONVROT_LAYOUT_MFMA: the format the GEMMs stream.  Rows are grouped in blocks of 32 (NB = ceil(N/32)
- *    blocks, rows past N are zero); every (row block nb, K-block) is one contiguous 1 KiB tile laid out in
- *    the lane order of the gfx950 v_mfma_i32_32x32x32_i8 B operand, so that a wavefront fetches it with one
- *    coalesced 16-byte load per lane.  With r = n % 32:
+ *    blocks, rows past N are zero); every (row block nb, K-block) is one contiguous 1 KiB tile, so that a
+ *    wavefront fetches it with one coalesced 16-byte load per lane, laid out so that the gfx950 int8 MFMA
+ *    operand fragments (16 rows by 16 consecutive k per lane) are read from LDS free of bank conflicts.
+ *    With r = n % 32:
  *      int8 (K-blocks of 32):  byte ((nb*(K/32) + k/32)*1024 + (r + 32*((k%32)/16))*16 + k%16)
- *      int4 (K-blocks of 64):  byte ((nb*(K/64) + k/64)*1024 + (r + 32*((k%32)/16))*16 + 8*((k%64)/32)
+ *      int4 (K-blocks of 64):  byte ((nb*(K/64) + k/64)*1024 + (64*(r/16) + 16*((k%64)/16) + r%16)*8
  *                                    + 4*((k%16)/8) + k%4), low nibble if k%8 < 4, else high nibble (each
  *                                    4-byte word: k..k+3 in the low nibbles, k+4..k+7 in the high ones);
  *                                    requires K % 64 == 0.

@@ -43,20 +43,20 @@ def say(msg: str):
 
 def untile_codes(buf: np.ndarray, E: int, N: int, K: int, bits: int) -> np.ndarray:
     """Row-major codes (int8 [E, N, K]) from a buffer in the MFMA-tiled layout documented in include/convrot.h:
-    rows in blocks of 32 (padded), each (row block, K-block) tile 1 KiB, lane L = r + 32*((k%32)/16) holding
-    16 consecutive k (int8), or for int4 two 8-byte halves (k%64 < 32, >= 32) of 16 nibbles each; in each
-    4-byte word the low nibbles hold 4 consecutive k and the high nibbles the next 4."""
+    rows in blocks of 32 (padded), each (row block, K-block) tile 1 KiB; int8: lane L = r + 32*((k%32)/16)
+    holding 16 consecutive k; int4: 8-byte entry 64*(r/16) + 16*((k%64)/16) + r%16 holding 16 consecutive k,
+    in each 4-byte word the low nibbles 4 consecutive k and the high nibbles the next 4."""
     NB = (N + 31) // 32
     b = np.ascontiguousarray(buf).view(np.uint8)
     if bits == 8:
         t = b.view(np.int8).reshape(E, NB, K // 32, 2, 32, 16)        # e, nb, ks, half, r, j
         codes = t.transpose(0, 1, 4, 2, 3, 5).reshape(E, NB * 32, K)  # e, nb, r, ks, half, j
     else:
-        t = b.reshape(E, NB, K // 64, 2, 32, 2, 2, 4)                  # e, nb, ks2, half, r, sl, word, byte
-        lo = (t & 0xF).astype(np.int8)                                 # k = 8 word + byte
-        hi = (t >> 4).astype(np.int8)                                  # k = 8 word + 4 + byte
+        t = b.reshape(E, NB, K // 64, 2, 4, 16, 2, 4)                  # e, nb, ks, r/16, (k%64)/16, r%16, word, byte
+        lo = (t & 0xF).astype(np.int8)                                 # k%16 = 8 word + byte
+        hi = (t >> 4).astype(np.int8)                                  # k%16 = 8 word + 4 + byte
         lo = np.where(lo >= 8, lo - 16, lo)
         hi = np.where(hi >= 8, hi - 16, hi)
-        nib = np.stack([lo, hi], axis=-2).reshape(E, NB, K // 64, 2, 32, 2, 16)  # ..., sl, j
-        codes = nib.transpose(0, 1, 4, 2, 5, 3, 6).reshape(E, NB * 32, K)          # e, nb, r, ks2, sl, half, j
+        nib = np.stack([lo, hi], axis=-2).reshape(E, NB, K // 64, 2, 4, 16, 16)  # ..., k%16
+        codes = nib.transpose(0, 1, 3, 5, 2, 4, 6).reshape(E, NB * 32, K)          # e, nb, r/16, r%16, ks, g, j
     return np.ascontiguousarray(codes[:, :N, :]).astype(np.int8)

@@ -25,8 +25,9 @@
 //     gathered activation rows, the per-tile row indices, row scales and column scales.
 //   * Weights are stored MFMA-tiled: each (32-row block, K-block) tile is 1 KiB in lane order, so a DMA is one
 //     coalesced 16-byte load per lane (non-temporal: each byte is used once) and a fragment read is one
-//     ds_read_b128 (ds_read_b64 and an unpack for 4-bit weights).  Activation rows are 64 bytes per stage with the 16-byte chunks XOR-swizzled by
-//     (row / 4) % 4, so the fragment reads are free of bank conflicts.
+//     ds_read_b128 (ds_read_b64 and an unpack for 4-bit weights).  Activation rows are 64 bytes per stage, placed
+//     within each 16-row block and chunk-swizzled so that the fragment reads are free of bank conflicts (the
+//     layout is described at a_pos_of_row).
 //   * Load roles: wavefronts 0-3 issue the weight DMAs into an SB-deep ring, wavefronts 4-7 the activation
 //     DMAs into an SA-deep ring.  A wavefront's vector memory operations complete in issue order, so waiting
 //     for vmcnt <= X, where X counts operations it issued after a stage, proves that the stage has landed.
@@ -85,8 +86,15 @@ __device__ __forceinline__ uint2 unpack_nibbles(uint32_t w) {
     return r;
 }
 
-// LDS byte offset of 16-byte chunk c (0..3) of 64-byte row r: activation stages and epilogue staging blocks.
-__device__ __forceinline__ int swz_offset(int r, int c) { return r * kBK + ((c ^ ((r >> 2) & 3)) << 4); }
+// Activation stage layout: each 16-row block is 1 KiB of 16 positions of 64 bytes.  Row r of the block sits at
+// position a_pos_of_row(r), its 16-byte chunk c at slot c ^ ((r >> 1) & 3) of the position.  A fragment read
+// (lane l: row l % 16, chunk l / 16) is served 16 lanes per LDS cycle, as two groups of 8 lanes that must each
+// fall in one 128-byte half of a 256-byte bank line, on distinct 16-byte slots, and the two groups in opposite
+// halves: rows 0-7 land on positions with (p & 2) == 0, rows 8-15 on (p & 2) == 2, and the four rows of a
+// group that share a half and a slot column get four different chunk slots.  The DMA side keeps four
+// consecutive lanes on one 64-byte row piece, so each row of a stage is still one coalesced request.
+__device__ __forceinline__ int a_pos_of_row(int r) { return 4 * ((r >> 1) & 3) + 2 * (r >> 3) + (r & 1); }
+__device__ __forceinline__ int a_row_of_pos(int q) { return 8 * ((q >> 1) & 1) + 2 * (q >> 2) + (q & 1); }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] in bits 15:14).
@@ -278,9 +286,10 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
                 src[j] = p.A;
                 src_off[j] = 0;
                 if (j >= NAW) continue;
-                const int slot = (4 * j + aw) * 64 + lane;
-                const int r = slot >> 2;                    // tile row
-                const int c = (slot & 3) ^ ((r >> 2) & 3);  // logical 16-byte chunk held by that slot
+                // 16-byte slot `lane` of the 1 KiB block 4 j + aw (16 tile rows): position lane / 4 holds row
+                // a_row_of_pos(lane / 4) of the block, its chunk (lane & 3) ^ ((lane >> 4) & 3)
+                const int r = (4 * j + aw) * 16 + a_row_of_pos(lane >> 2);  // tile row
+                const int c = (lane & 3) ^ ((lane >> 4) & 3);               // logical 16-byte chunk
                 src[j] = p.A + arow_of(r) * K;
                 src_off[j] = c * 16;
             }
@@ -350,12 +359,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     constexpr int MH = MS / 2;
     static_assert(MH >= 1, "half steps need two token blocks per wavefront");
     const int g4 = lane >> 4;  // the lane's k chunk; in the result, its 4-column group of each 16-column block
-    // per-lane byte offsets inside a stage: weight fragment (q, s) of block blk is at b_lane + (2 blk) KiB
-    // (int8: two 1 KiB tiles per 64 k, the chunk's tile g4 / 2) or b_lane + blk KiB (int4: one tile, 8-byte
-    // half g4 / 2), + 256 s; token block m at a_lane + (m * 16 + the half's first row) * 64 (swizzled chunks)
-    const int b_lane = (WBITS == 8) ? ((lane & 15) + 32 * (g4 & 1)) * 16 + 1024 * (g4 >> 1)
-                                    : ((lane & 15) + 32 * (g4 & 1)) * 16 + 8 * (g4 >> 1);
-    const int a_lane = (lane & 15) * kBK + ((g4 ^ ((lane >> 2) & 3)) << 4);
+    // per-lane byte offsets inside a stage: weight fragment (q, s) of block blk is at b_lane + (2 blk) KiB +
+    // 256 s (int8: two 1 KiB tiles per 64 k, the chunk's tile g4 / 2) or b_lane + blk KiB + 512 s (int4: one
+    // tile, the fragment's 64 lanes on 512 contiguous bytes); token block m at a_lane + (m * 16 + the half's
+    // first row) * 64 (placed and swizzled rows)
+    const int b_lane = (WBITS == 8) ? ((lane & 15) + 32 * (g4 & 1)) * 16 + 1024 * (g4 >> 1) : lane * 8;
+    const int a_lane = a_pos_of_row(lane & 15) * kBK + ((g4 ^ ((lane >> 1) & 3)) << 4);
 
     v4i acc[MS][2][2];
     auto clear_acc = [&]() {
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     };
     auto read_b = [&](int bs, int q, int s) -> v4i {
         const int blk = q ? my_blk1 : my_blk0;
-        const int8_t* p = b_ring + bs * B_BYTES + b_lane + 256 * s;
+        const int8_t* p = b_ring + bs * B_BYTES + b_lane + (WBITS == 8 ? 256 : 512) * s;
         if constexpr (WBITS == 8) {
             return *reinterpret_cast<const v4i*>(p + 2048 * blk);
         } else {

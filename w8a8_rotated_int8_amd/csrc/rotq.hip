@@ -66,15 +66,17 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 }
 
 // Byte offset of the 8 codes k = 8i .. 8i+7 of row n (of one expert) in the MFMA-tiled layout: every
-// (32-row block, K-block) tile is 1 KiB in the lane order of the v_mfma_i32_32x32x32_i8 B operand (lane
-// r + 32*((k%32)/16) holds 16 consecutive k); int4 tiles span 64 k and hold two 8-byte halves per lane.
+// (32-row block, K-block) tile is 1 KiB.  int8 tiles span 32 k: 16-byte entry r + 32*((k%32)/16) holds 16
+// consecutive k of row r.  int4 tiles span 64 k: 8-byte entry 64*(r/16) + 16*((k%64)/16) + r%16 holds 16
+// consecutive k of row r, so the 64 lanes of a 16-row fragment read 512 contiguous bytes.
 template <bool INT4>
 __device__ __forceinline__ int64_t tiled_offset(int n, int k, int K) {
-    const int r = n & 31, lane = r + 32 * ((k & 31) >> 4);
+    const int r = n & 31;
     if constexpr (!INT4) {
-        return ((int64_t)(n >> 5) * (K >> 5) + (k >> 5)) * 1024 + lane * 16 + (k & 15);
+        return ((int64_t)(n >> 5) * (K >> 5) + (k >> 5)) * 1024 + (r + 32 * ((k & 31) >> 4)) * 16 + (k & 15);
     } else {
-        return ((int64_t)(n >> 5) * (K >> 6) + (k >> 6)) * 1024 + lane * 16 + 8 * ((k & 63) >> 5) + ((k & 15) >> 1);
+        return ((int64_t)(n >> 5) * (K >> 6) + (k >> 6)) * 1024 + (64 * (r >> 4) + 16 * ((k & 63) >> 4) + (r & 15)) * 8 +
+               ((k & 15) >> 1);
     }
 }
 
