@@ -423,6 +423,8 @@ def main():
     ap.add_argument("--dense-shape", default="qkv", choices=["qkv", "ffn_down", "out"])
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="single-layer workloads: steps timed one by one after a 1 GiB scratch write (0 skips)")
+    ap.add_argument("--fused-rounds", type=int, default=4,
+                    help="rounds of the one-launch expert path against the default (0: skip)")
     ap.add_argument("--stack-layers", type=int, default=29,
                     help="config 3: also time the weight-streaming stack of this many layers with 8- and 4-bit "
                          "weights (0 skips)")
@@ -631,6 +633,29 @@ def run_moe(args):
                         "frac_hbm_peak": round(lbytes / (cu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                         "steps": args.cold_steps, "note": "median over steps, each after a 1 GiB scratch write"}
         print(f"bench: cold {cu:.1f} us/layer (median of {args.cold_steps})", file=sys.stderr, flush=True)
+    if n_layers == 1 and args.fused_rounds > 0 and cr.moe_expert_choice_fused(w, s.C):
+        # the one-launch expert path against the default three launches, alternating blocks of 10 steps so that
+        # both see the same clock
+        def block(fused):
+            e0, e1 = _events(2)
+            e0.record(stream)
+            for _ in range(10):
+                cr.moe_expert_choice_forward(xd, layers[0][0], s.C, w, out=out, idx_out=idx, wt_out=wt, ws=ws,
+                                             stream=stream, fused=fused)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / 10
+        res = {False: [], True: []}
+        block(True)
+        for r in range(args.fused_rounds):
+            for fz in ((False, True) if r % 2 == 0 else (True, False)):
+                res[fz].append(block(fz))
+        f_us, t_us = float(np.median(res[True])), float(np.median(res[False]))
+        line["fused_experts"] = {"us_per_layer": round(f_us, 2), "three_launches_us_per_layer": round(t_us, 2),
+                                 "note": "moe_expert_choice_forward_fused against moe_expert_choice_forward, "
+                                         "median of alternating 10-step blocks"}
+        print(f"bench: one-launch experts {f_us:.1f} us/layer, three launches {t_us:.1f} us/layer",
+              file=sys.stderr, flush=True)
     if args.config == 3 and args.stack_layers > 0:
         st4 = synth.CONFIGS[4]
         line["stack"] = {"layers": args.stack_layers,

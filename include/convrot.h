@@ -184,6 +184,27 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
                                          const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
                                          float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_expert_choice_forward with the hidden rows' rotate+quantise fused with the two grouped GEMMs into one
+ * persistent launch ("MLX Nucleus-Image", "Conversion notes": the expert FFN; "Nucleus-Image INT8 Convrot
+ * Experts + FP8 Text Encoder", "Quantization": group 64 for the down projection's input).  Same arguments,
+ * workspace and results, bit for bit.  The launch runs one workgroup per CU through three phases: the gate/up
+ * tiles, then rotate+quantise of the hidden rows of every expert whose gate/up tiles are all done, then the
+ * down tiles of every expert whose rows are all done, ordered through per-expert counters in the workspace
+ * (a row's scale needs all of its I columns, which come from several CUs, so the quantisation cannot sit in
+ * the gate/up epilogue itself).  It needs every one of its workgroups resident at once: a kernel of another
+ * stream that holds CUs delays it, and one holding them for more than about a second per wait leaves wrong
+ * results (the waits are bounded; the launch always finishes).  On MI355X it is slower than the three
+ * launches of moe_expert_choice_forward, whose kernel boundaries cost next to nothing.
+ * CONVROT_ERR_SHAPE where moe_expert_choice_fused(w, C) is 0; other errors as moe_expert_choice_forward. */
+convrot_status moe_expert_choice_forward_fused(const uint16_t* x, int T, const float* router_logits, int C,
+                                               const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                               float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* 1 if moe_expert_choice_forward_fused takes a layer with these weights and C, else 0 (also for invalid
+ * arguments).  Shapes only; no GPU call: group_dn = 64 with I in {512, 1024, 1536, 2048}, or group_dn = 256
+ * with I = 2048, for either weight width. */
+int moe_expert_choice_fused(const convrot_moe_weights* w, int C);
+
 /* Size of the static scratch the allocation-free forward uses: 192 MiB per GPU (the T = 8192, C = 256 layer
  * with E = 64, d = 2048, I = 1536 takes 163.8 MB of it). */
 #define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)

@@ -18,7 +18,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = cr.header_functions()
-    assert len(names) == 26
+    assert len(names) == 28
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cr._SIGS)
@@ -113,6 +113,30 @@ def test_moe_forward_validation(L):
     assert f(*args(ww=_weights(s_gu=P + 4))) == ALIGN
     assert f(*args(ww=_weights(I=1568))) == GROUP  # 1568 is not a multiple of the down group 64
     assert f(None, 8192, P, 256, ctypes.byref(w), P, None, None, P, need, None) == NULL
+
+
+def test_moe_fused_query(L):
+    """Which layers the one-launch forward (gate/up, the hidden rows' rotate+quantise, down) takes."""
+    f = L.moe_expert_choice_fused
+    for bits in (8, 4):
+        assert f(ctypes.byref(_weights(wbits=bits)), 256) == 1  # T = 8192 layer: I = 1536, group 64
+        assert f(ctypes.byref(_weights(wbits=bits)), 1024) == 1  # several M-blocks per expert
+    assert f(ctypes.byref(_weights(I=512)), 37) == 1
+    assert f(ctypes.byref(_weights(I=2048, group_dn=256)), 8) == 1
+    assert f(ctypes.byref(_weights(I=1024, group_dn=256)), 8) == 0  # group 256 only with I = 2048
+    assert f(ctypes.byref(_weights(I=128)), 24) == 0   # rows too short: three launches
+    assert f(ctypes.byref(_weights(I=2560)), 24) == 0  # five 512-element rounds: three launches
+    assert f(ctypes.byref(_weights(wbits=3)), 24) == 0
+    assert f(ctypes.byref(_weights()), 0) == 0
+    assert f(None, 256) == 0
+    g = L.moe_expert_choice_forward_fused
+    w = _weights()
+    need = L.moe_expert_choice_workspace_bytes(8192, 256, ctypes.byref(w))
+    args = lambda C=256, ww=w, nb=need: (P, 8192, P, C, ctypes.byref(ww), P, None, None, P, nb, None)
+    assert g(*args(ww=_weights(I=128))) == SHAPE
+    assert g(*args(nb=need - 1)) == WS
+    assert g(*args(C=0)) == SHAPE
+    assert g(None, 8192, P, 256, ctypes.byref(w), P, None, None, P, need, None) == NULL
 
 
 def test_stage_validation(L):

@@ -63,6 +63,11 @@ def _check_layer(x, lg, w_gu_d, w_dn_d, w_gu, w_dn, shape, bits, what):
     exact = assert_bf16_within(host_bf16(out), ref["out"], what=f"{what} out")
     say(f"{what}: layer output {exact * 100:.3f}% bit-identical")
     assert exact == 1.0
+    if cr.moe_expert_choice_fused(w, s.C):
+        say(f"{what}: GPU layer, one-launch expert path")
+        out_f, _, _ = cr.moe_expert_choice_forward(xd, lgd, s.C, w, fused=True)
+        assert torch.equal(out_f.view(torch.int16), out.view(torch.int16)), "one-launch layer output"
+        del out_f
 
     say(f"{what}: stages from the oracle's inputs")
     qx, sx, _ = cr.convrot_rotq_rows(xd, s.g_gu)

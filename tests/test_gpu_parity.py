@@ -351,6 +351,39 @@ def test_moe_forward_end_to_end(si, bits):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+# Shapes that the one-launch expert path (gate/up, hidden-row rotate+quantise, down) takes: each rotation variant
+# of the hidden rows (group 64 with I / 512 = 1, 2, 3, 4; group 256 with I = 2048), the three tile heights
+# (C <= 64, <= 128, > 128, and two M-blocks per expert), an expert count that the 8 XCDs do not divide, and a
+# grid of fewer than 8 workgroups.
+FUSED = [
+    synth.MoEShape(T=300, d=512, E=6, I=512, C=37, g_gu=256, g_dn=64),
+    synth.MoEShape(T=400, d=256, E=5, I=1024, C=100, g_gu=256, g_dn=64),
+    synth.MoEShape(T=64, d=512, E=9, I=1536, C=8, g_gu=64, g_dn=64),
+    synth.MoEShape(T=600, d=512, E=3, I=2048, C=300, g_gu=256, g_dn=256),
+    synth.MoEShape(T=200, d=256, E=2, I=2048, C=130, g_gu=64, g_dn=64),
+    synth.MoEShape(T=2, d=512, E=1, I=512, C=1, g_gu=256, g_dn=64),
+]
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("si", range(len(FUSED)))
+def test_moe_forward_fused_bit_exact(si, bits):
+    shape = FUSED[si]
+    say(f"moe forward, one expert launch {shape} bits={bits}")
+    x, lg, w, ref = _layer(shape, bits, 30000 + si)
+    assert cr.moe_expert_choice_fused(w, shape.C)
+    out, idx, wt = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w, fused=True)
+    assert np.array_equal(host(idx), ref["idx"])
+    assert np.array_equal(host(wt).view(np.uint32), ref["wt"].view(np.uint32))
+    assert np.array_equal(host_bf16(out), ref["out"]), "moe out"
+    # the counters are cleared by every call's selection: further calls, also after a three-launch forward on
+    # the same workspace, give the same bits
+    ws = torch.empty(cr.moe_expert_choice_workspace_bytes(shape.T, shape.C, w), dtype=torch.uint8, device=DEV)
+    for fused in (True, False, True):
+        o, _, _ = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w, ws=ws, fused=fused)
+        assert torch.equal(out.view(torch.int16), o.view(torch.int16)), f"repeat (fused={fused})"
+
+
 def test_single_expert_ffn_config1():
     """One routed-expert SwiGLU FFN without routing (E = 1, C = T = 1024, d = 2048, I = 1536)."""
     shape = synth.CONFIGS[1]
@@ -366,6 +399,15 @@ def test_single_expert_ffn_config1():
     assert np.array_equal(host(idx), ref["idx"]) and np.all(host(wt) == 1.0)
     exact = assert_bf16_within(host_bf16(out), ref["out"], what="config 1 out")
     assert exact == 1.0
+
+
+def test_moe_forward_fused_rejects_other_shapes():
+    shape = SMALL[0]  # I = 128: rows too short for the one-launch path
+    x, lg, w_gu, w_dn = synth.moe_inputs(2, shape, seed_base=40000)
+    w = cr.quantize_moe_weights(dev_bf16(w_gu), dev_bf16(w_dn), shape.g_gu, shape.g_dn, 8)
+    assert not cr.moe_expert_choice_fused(w, shape.C)
+    with pytest.raises(cr.ConvrotError, match="SHAPE"):
+        cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w, fused=True)
 
 
 def test_moe_forward_without_routing_outputs():

@@ -47,6 +47,8 @@ _SIGS = {
     "convrot_linear_workspace_bytes": (_sz, [_i, _i]),
     "convrot_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _sz, _p]),
     "moe_expert_choice_workspace_bytes": (_sz, [_i, _i, ctypes.POINTER(ConvrotMoeWeightsC)]),
+    "moe_expert_choice_fused": (_i, [ctypes.POINTER(ConvrotMoeWeightsC), _i]),
+    "moe_expert_choice_forward_fused": (_i, [_p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p, _p, _p, _sz, _p]),
     "moe_expert_choice_forward": (_i, [_p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p, _p, _p, _sz, _p]),
     "moe_expert_choice_forward_noalloc": (_i, [_p, _i, _p, _i, ctypes.POINTER(ConvrotMoeWeightsC), _p, _p, _p, _p]),
     "convrot_rotq_rows": (_i, [_p, _i64, _i, _i, _p, _p, _p, _p]),
@@ -216,11 +218,18 @@ def moe_expert_choice_workspace_bytes(T: int, C: int, w: MoeWeights) -> int:
     return lib().moe_expert_choice_workspace_bytes(T, C, ctypes.byref(cw))
 
 
+def moe_expert_choice_fused(w: MoeWeights, C: int) -> bool:
+    """Whether moe_expert_choice_forward_fused takes this layer."""
+    cw = w.c_struct()
+    return bool(lib().moe_expert_choice_fused(ctypes.byref(cw), C))
+
+
 def moe_expert_choice_forward(x, router_logits, C: int, w: MoeWeights, out=None, idx_out=None, wt_out=None,
-                              ws=None, stream=None, want_routing: bool = True):
+                              ws=None, stream=None, want_routing: bool = True, fused: bool = False):
     """Routed-expert MoE layer.  Returns (out [T, d] bf16, idx [E, C] int32, wt [E, C] fp32); with
     want_routing=False and no idx_out / wt_out given, the routing outputs are not written (NULL) and come back
-    as None."""
+    as None.  fused=True calls moe_expert_choice_forward_fused (the expert GEMMs and the hidden rows'
+    rotate+quantise in one launch; same results)."""
     T, d = x.shape
     if out is None:
         out = _empty((T, d), torch.bfloat16, x)
@@ -231,7 +240,8 @@ def moe_expert_choice_forward(x, router_logits, C: int, w: MoeWeights, out=None,
     cw = w.c_struct()
     nbytes = lib().moe_expert_choice_workspace_bytes(T, C, ctypes.byref(cw))
     ws = _workspace(nbytes, x, ws)
-    _check("moe_expert_choice_forward", lib().moe_expert_choice_forward(
+    name = "moe_expert_choice_forward_fused" if fused else "moe_expert_choice_forward"
+    _check(name, getattr(lib(), name)(
         _ptr(x), T, _ptr(router_logits), C, ctypes.byref(cw), _ptr(out), _ptr(idx_out), _ptr(wt_out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
     return out, idx_out, wt_out

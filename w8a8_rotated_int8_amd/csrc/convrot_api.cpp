@@ -18,6 +18,7 @@ constexpr int kRotqBesideSoftmaxPct = 25;  // share of the token rows rotated in
 constexpr int kMaxRowLen = 8192;           // rotate/quantise keeps a row in registers of one wavefront
 constexpr int64_t kMaxKInt32 = 131056;     // K * 128^2 < 2^31 for any int8 codes (-128 included), K % 16 == 0
 
+
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -51,6 +52,7 @@ struct MoeBuffers {
     int8_t* qa;
     float* sa;
     uint16_t* z;
+    uint32_t* esync;  // per-expert counters of the fused expert launch
 };
 
 size_t plan_moe(void* ws, int T, int C, const convrot_moe_weights& w, MoeBuffers* b) {
@@ -68,6 +70,7 @@ size_t plan_moe(void* ws, int T, int C, const convrot_moe_weights& w, MoeBuffers
     m.qa = cv.take<int8_t>(S * w.I);
     m.sa = cv.take<float>(S);
     m.z = cv.take<uint16_t>(S * w.d);
+    m.esync = cv.take<uint32_t>((size_t)2 * w.E * crk::kEsyncStride);
     if (b) *b = m;
     return cv.used;
 }
@@ -158,9 +161,11 @@ convrot_status check_forward(const uint16_t* x, int T, const float* router_logit
 // The forward's launch sequence on a validated call; ws holds at least plan_moe(T, C, w) bytes.  Every
 // workspace byte a launch reads was written by an earlier launch of the same call, so ws need not start
 // cleared.
+// fused: gate/up, rotate + quantise of the hidden rows and down as one persistent launch (the caller has checked
+// that the shapes allow it); else three launches.
 convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_logits, int C,
                                const convrot_moe_weights& w, uint16_t* out, int32_t* idx_out, float* wt_out,
-                               void* ws, hipStream_t stream) {
+                               void* ws, bool fused, hipStream_t stream) {
     MoeBuffers b;
     plan_moe(ws, T, C, w, &b);
     int32_t* idx = idx_out ? idx_out : b.idx;
@@ -175,15 +180,21 @@ convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_log
         CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, b.tokmask, x, w.d, w.group_gu, b.qx, b.sx,
                                          t1, stream));
         CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, x, w.d, w.group_gu, b.qx,
-                                        b.sx, t1, stream));
+                                        b.sx, t1, b.esync, stream));
     } else {
         CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, b.tokmask, stream));
         CRK_TRY(crk::launch_rotq_act(x, T, w.d, w.group_gu, b.qx, b.sx, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, stream));
+        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, b.esync, stream));
     }
-    CRK_TRY(crk::launch_grouped_gemm(gateup_problem(b.qx, b.sx, T, idx, C, w, b.a), stream));
-    CRK_TRY(crk::launch_rotq_act(b.a, S, w.I, w.group_dn, b.qa, b.sa, nullptr, stream));
-    CRK_TRY(crk::launch_grouped_gemm(down_problem(b.qa, b.sa, C, w, b.z), stream));
+    const crk::GemmProblem gu = gateup_problem(b.qx, b.sx, T, idx, C, w, b.a);
+    const crk::GemmProblem dn = down_problem(b.qa, b.sa, C, w, b.z);
+    if (fused) {
+        CRK_TRY(crk::launch_moe_experts(gu, dn, b.a, b.qa, b.sa, w.group_dn, b.esync, stream));
+    } else {
+        CRK_TRY(crk::launch_grouped_gemm(gu, stream));
+        CRK_TRY(crk::launch_rotq_act(b.a, S, w.I, w.group_dn, b.qa, b.sa, nullptr, stream));
+        CRK_TRY(crk::launch_grouped_gemm(dn, stream));
+    }
     CRK_TRY(crk::launch_combine(b.z, b.slotmap, b.tokmask, wt, T, w.E, C, w.d, out, stream));
     return CONVROT_OK;
 }
@@ -381,6 +392,16 @@ convrot_status convrot_linear_g16(const uint16_t* x, int M, int K, const uint8_t
     return CONVROT_OK;
 }
 
+int moe_expert_choice_fused(const convrot_moe_weights* w, int C) {
+    if (!w || C < 1 || w->E < 1 || w->d < 1 || w->I < 1) return 0;
+    if (w->wbits != 8 && w->wbits != 4) return 0;
+    if ((int64_t)w->E * C > INT32_MAX || (int64_t)w->E * 2 * w->I > INT32_MAX) return 0;
+    return crk::moe_experts_supported(gateup_problem(nullptr, nullptr, C, nullptr, C, *w, nullptr),
+                                      down_problem(nullptr, nullptr, C, *w, nullptr), w->group_dn)
+               ? 1
+               : 0;
+}
+
 size_t moe_expert_choice_workspace_bytes(int T, int C, const convrot_moe_weights* w) {
     if (!w || T < 1 || C < 1 || w->E < 1 || w->d < 1 || w->I < 1) return 0;
     return plan_moe(nullptr, T, C, *w, nullptr);
@@ -393,7 +414,17 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
     if (st != CONVROT_OK) return st;
     if (!ws || ws_bytes < plan_moe(nullptr, T, C, *w, nullptr)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
-    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, stream);
+    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, false, stream);
+}
+
+convrot_status moe_expert_choice_forward_fused(const uint16_t* x, int T, const float* router_logits, int C,
+                                               const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
+                                               float* wt_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const convrot_status st = check_forward(x, T, router_logits, C, w, out, idx_out, wt_out);
+    if (st != CONVROT_OK) return st;
+    if (!moe_expert_choice_fused(w, C)) return CONVROT_ERR_SHAPE;
+    if (!ws || ws_bytes < plan_moe(nullptr, T, C, *w, nullptr)) return CONVROT_ERR_WORKSPACE;
+    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, true, stream);
 }
 
 convrot_status moe_expert_choice_forward_noalloc(const uint16_t* x, int T, const float* router_logits, int C,
@@ -404,7 +435,7 @@ convrot_status moe_expert_choice_forward_noalloc(const uint16_t* x, int T, const
     if (plan_moe(nullptr, T, C, *w, nullptr) > CONVROT_NOALLOC_SCRATCH_BYTES) return CONVROT_ERR_WORKSPACE;
     void* ws = nullptr;
     if (scratch_of_current_device(&ws) != hipSuccess) return CONVROT_ERR_HIP;
-    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, stream);
+    return enqueue_forward(x, T, router_logits, C, *w, out, idx_out, wt_out, ws, false, stream);
 }
 
 convrot_status convrot_rotq_rows(const uint16_t* x, int64_t rows, int K, int group, int8_t* q_out, float* s_out,
@@ -473,7 +504,7 @@ convrot_status moe_route_expert_choice(const float* in, int is_probs, int T, int
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
     float* probs_t = static_cast<float*>(ws);
     CRK_TRY(crk::launch_softmax_t(in, is_probs ? 1 : 0, T, E, probs_t, probs_out, nullptr, stream));
-    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, nullptr, stream));
+    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, nullptr, nullptr, stream));
     return CONVROT_OK;
 }
 

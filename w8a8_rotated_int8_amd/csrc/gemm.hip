@@ -44,11 +44,13 @@
 //     before its first use.
 // INT32 accumulation is exact, so the result does not depend on the k order inside the MFMA.  4-bit weights
 // are sign-extended to int8 in registers right before the MFMA.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
+#include "rotq_fast.h"
 
 namespace crk {
 namespace {
@@ -158,8 +160,27 @@ struct GemmCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+// Split of `total` work items over G workgroups: XCD x (the workgroups with wg % 8 == x) owns the contiguous range
+// [xs, xs + xn) of the items, and its workgroups take the items of that range round robin.  Below 8 workgroups
+// each one is its own group, so that every item still has an owner.
+struct XcdSplit {
+    int xs, local, nwg_x, count;
+    __device__ __forceinline__ XcdSplit(int total, int G, int wg) {
+        const int nx = G < 8 ? G : 8;
+        const int xcd = wg % nx;
+        local = wg / nx;
+        nwg_x = (G - xcd + nx - 1) / nx;
+        const int base = total / nx, extra = total % nx;
+        xs = xcd * base + (xcd < extra ? xcd : extra);
+        const int xn = base + (xcd < extra ? 1 : 0);
+        count = local < xn ? (xn - local + nwg_x - 1) / nwg_x : 0;
+    }
+    __device__ __forceinline__ int item(int i) const { return xs + local + i * nwg_x; }  // i-th item here
+};
+
+// The tiles of one grouped GEMM that the split gives this workgroup (all 8 wavefronts call it).
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmProblem p, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void gemm_tiles(const GemmProblem& p, int tiles_m, int tiles_n, const XcdSplit split) {
     using Cfg = GemmCfg<BM, SB, SA, EPI, WBITS, TILED>;
     constexpr int NBW = Cfg::NBW, NAW = Cfg::NAW;
     constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
@@ -174,7 +195,10 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     int32_t* const rows_lds = reinterpret_cast<int32_t*>(smem + Cfg::ROWS_OFF);
     float* const silu_lds = reinterpret_cast<float*>(smem + Cfg::SILU_OFF);
 
-    const int tid = threadIdx.x;
+    // The thread index passes through an empty asm statement, so that where two of these bodies run in one
+    // kernel nothing derived from it is computed once and kept live across both.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches stay scalar
     const int mh = wave >> 2;  // M-half computed by this wavefront
@@ -189,20 +213,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
     // with the first stage of tile i, is published by the time tile i+1's loads are issued (nk >= SA).
     const bool rows_via_lds = p.a_rows != nullptr && nk >= SA;
 
-    // ---- this workgroup's tiles: XCD x owns the contiguous range [xs, xs + xn); its workgroups interleave ----
-    const int total = p.E * tiles_m * tiles_n;
-    const int G = (int)gridDim.x;
-    const int xcd = (int)blockIdx.x % 8, local = (int)blockIdx.x / 8;
-    const int nwg_x = (G - xcd + 7) / 8;
-    const int base = total / 8, extra = total % 8;
-    const int xs = xcd * base + (xcd < extra ? xcd : extra);
-    const int xn = base + (xcd < extra ? 1 : 0);
-    const int my_tiles = local < xn ? (xn - local + nwg_x - 1) / nwg_x : 0;
+    // ---- this workgroup's tiles ----
+    const int my_tiles = split.count;
     if (my_tiles == 0) return;  // workgroup-uniform
     const int total_stages = my_tiles * nk;
     // M-blocks fastest, then N-tiles, then experts
     auto decode = [&](int i, int& e, int& nt, int& mt) {
-        const int t = xs + local + i * nwg_x;
+        const int t = split.item(i);
         mt = t % tiles_m;
         nt = (t / tiles_m) % tiles_n;
         e = t / (tiles_m * tiles_n);
@@ -704,6 +721,30 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmPro
 }
 
 template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(const GemmProblem p, int tiles_m, int tiles_n) {
+    gemm_tiles<BM, SB, SA, EPI, WBITS, TILED>(p, tiles_m, tiles_n,
+                                              XcdSplit(p.E * tiles_m * tiles_n, (int)gridDim.x, (int)blockIdx.x));
+}
+
+// Compute units of the current device, looked up once per device (calls from several threads may race to store
+// the same value).
+hipError_t device_cus(int* ncu) {
+    static std::atomic<int> ncu_cache[64];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    int n = (dev >= 0 && dev < 64) ? ncu_cache[dev].load(std::memory_order_relaxed) : 0;
+    if (n <= 0) {
+        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        if (n <= 0) return hipErrorInvalidValue;
+        if (dev >= 0 && dev < 64) ncu_cache[dev].store(n, std::memory_order_relaxed);
+    }
+    *ncu = n;
+    return hipSuccess;
+}
+
+template <int BM, int SB, int SA, Epi EPI, int WBITS, bool TILED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
     using Cfg = GemmCfg<BM, SB, SA, EPI, WBITS, TILED>;
     const int tiles_m = (p.M + BM - 1) / BM;
@@ -717,18 +758,9 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
     if (total > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t ldo = (EPI == Epi::kSwiGLU) ? p.N / 2 : p.N;
     if ((int64_t)BM * ldo * 2 >= kOobOffset) return hipErrorInvalidValue;  // an output tile must fit one range
-    // compute units per device, looked up once (calls from several threads may race to store the same value)
-    static std::atomic<int> ncu_cache[64];
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    int ncu = 0;
+    const hipError_t err = device_cus(&ncu);
     if (err != hipSuccess) return err;
-    int ncu = (dev >= 0 && dev < 64) ? ncu_cache[dev].load(std::memory_order_relaxed) : 0;
-    if (ncu <= 0) {
-        err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err != hipSuccess) return err;
-        if (ncu <= 0) return hipErrorInvalidValue;
-        if (dev >= 0 && dev < 64) ncu_cache[dev].store(ncu, std::memory_order_relaxed);
-    }
     const int grid = (int)(total < ncu ? total : ncu);  // one persistent workgroup per CU
     kern<<<dim3((unsigned)grid), dim3(kThreads), Cfg::LDS, st>>>(p, tiles_m, tiles_n);
     return hipGetLastError();
@@ -751,6 +783,170 @@ hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
     }
 }
 
+// ---- the expert part of the MoE layer in one persistent launch -----------------------------------------
+// Three phases over the same workgroups, each split by XcdSplit, so that one expert's gate/up tiles, hidden rows
+// and down tiles fall on the same XCD (and its L2) when the experts divide evenly over the XCDs:
+//   1. the gate/up tiles with the SwiGLU epilogue, writing a;
+//   2. rotate + quantise of a's rows in items of 8 rows, one row per wavefront; an item first waits until
+//      every gate/up tile of its expert is published;
+//   3. the down tiles with the bf16 epilogue; they first wait until every item of their experts is published.
+// A workgroup publishes its tiles (or items) once it has finished all of them: every wavefront waits for its
+// own stores, the workgroup barrier, then one thread's agent-scope release fence and one atomic add per tile
+// or item on its expert's counter.  A wait is one thread polling the counter with relaxed agent-scope loads,
+// an agent-scope acquire fence, and the workgroup barrier.  Phase 1 waits for nothing and the grid holds at
+// most one workgroup per CU, all resident together, so every wait ends.  A poll still stops after kSpinLimit
+// rounds (about a second): that could only leave wrong results, never a launch that does not finish.
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target) {
+    for (int it = 0; it < kSpinLimit; ++it) {
+        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+        __builtin_amdgcn_s_sleep(40);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// All threads: publish the tiles or items of this workgroup, item i of the split counting once on counter
+// 2 (item / per_expert) + slot.
+__device__ __forceinline__ void publish(uint32_t* esync, int slot, const XcdSplit split, int per_expert) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0 && split.count > 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        for (int i = 0; i < split.count; ++i)
+            __hip_atomic_fetch_add(esync + (2 * (split.item(i) / per_expert) + slot) * kEsyncStride, 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+struct FusedExperts {
+    GemmProblem gu, dn;
+    const uint16_t* a;  // gu.out
+    int8_t* qa;         // dn.A
+    float* sa;          // dn.a_scale
+    int group;          // rotation group of a's rows
+    uint32_t* esync;    // counters (kEsyncStride apart): gate/up tiles of expert e at 2 e, its items at 2 e + 1
+};
+
+constexpr int kRowsInFlight = 8;
+
+// This wavefront's rows of the workgroup's rotate + quantise items (row 8 (item % nrb) + wave of expert
+// item / nrb), kRowsInFlight at a time: all their loads first, then each row's transform and stores.
+template <int G, int R>
+__device__ __forceinline__ void hidden_rows(const FusedExperts& f, const XcdSplit s2, int nrb, int wave) {
+    const int C = f.gu.M, I = f.gu.N >> 1;
+    for (int i0 = 0; i0 < s2.count; i0 += kRowsInFlight) {
+        RotqRaw<G, R> raw[kRowsInFlight];
+        int64_t row[kRowsInFlight];
+        bool ok[kRowsInFlight];
+#pragma unroll
+        for (int b = 0; b < kRowsInFlight; ++b) {
+            const int i = i0 + b;
+            const int j = i < s2.count ? s2.item(i) : 0, e = j / nrb, r = (j - e * nrb) * 8 + wave;
+            ok[b] = i < s2.count && r < C;  // wavefront-uniform
+            row[b] = (int64_t)e * C + r;
+            rotq_fast_load<G, R>(f.a, row[b], ok[b], I, 0, raw[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < kRowsInFlight; ++b)
+            if (ok[b]) rotq_fast_finish<G, R, 1>(raw[b], row[b], true, I, 0, f.qa, f.sa, nullptr);
+    }
+}
+
+template <int BM, int SBG, int SBD, int WBITS>
+__global__ __launch_bounds__(kThreads, 2) void moe_experts_kernel(const FusedExperts f, int tiles_n_gu, int tiles_n_dn) {
+    const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+    const int E = f.gu.E, C = f.gu.M, I = f.gu.N >> 1;
+    const int tiles_m = (C + BM - 1) / BM;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+
+    // phase 1: gate/up
+    const int gu_per_e = tiles_m * tiles_n_gu;
+    const XcdSplit s1(E * gu_per_e, G, wg);
+    gemm_tiles<BM, SBG, 3, Epi::kSwiGLU, WBITS, true>(f.gu, tiles_m, tiles_n_gu, s1);
+    publish(f.esync, 0, s1, gu_per_e);
+
+    // phase 2: rotate + quantise of the hidden rows, after every gate/up tile of the experts of this workgroup's
+    // items; wavefront w takes row 8 (item % nrb) + w of each item, with the loads of up to kRowsInFlight rows
+    // issued before any of them is transformed (one wavefront per SIMD pair would otherwise wait a full
+    // memory latency per row)
+    const int nrb = (C + 7) / 8;
+    const XcdSplit s2(E * nrb, G, wg);
+    if (threadIdx.x == 0) {
+        int last = -1;
+        for (int i = 0; i < s2.count; ++i) {
+            const int e = s2.item(i) / nrb;  // non-decreasing in i
+            if (e != last) wait_count(f.esync + (2 * e) * kEsyncStride, (uint32_t)gu_per_e);
+            last = e;
+        }
+    }
+    __syncthreads();
+    const int R = I / (8 * f.group);
+    if (f.group == 256)
+        hidden_rows<256, 1>(f, s2, nrb, wave);
+    else if (R == 1)
+        hidden_rows<64, 1>(f, s2, nrb, wave);
+    else if (R == 2)
+        hidden_rows<64, 2>(f, s2, nrb, wave);
+    else if (R == 3)
+        hidden_rows<64, 3>(f, s2, nrb, wave);
+    else
+        hidden_rows<64, 4>(f, s2, nrb, wave);
+    publish(f.esync, 1, s2, nrb);
+
+    // phase 3: down
+    const int dn_per_e = tiles_m * tiles_n_dn;
+    const XcdSplit s3(E * dn_per_e, G, wg);
+    if (threadIdx.x == 0) {
+        int last = -1;
+        for (int i = 0; i < s3.count; ++i) {
+            const int e = s3.item(i) / dn_per_e;  // non-decreasing in i
+            if (e != last) wait_count(f.esync + (2 * e + 1) * kEsyncStride, (uint32_t)nrb);
+            last = e;
+        }
+    }
+    __syncthreads();
+    gemm_tiles<BM, SBD, 3, Epi::kBf16, WBITS, true>(f.dn, tiles_m, tiles_n_dn, s3);
+}
+
+template <int BM, int SBG, int SBD, int WBITS>
+hipError_t launch_fused_cfg(const FusedExperts& f, hipStream_t st) {
+    using CG = GemmCfg<BM, SBG, 3, Epi::kSwiGLU, WBITS, true>;
+    using CD = GemmCfg<BM, SBD, 3, Epi::kBf16, WBITS, true>;
+    constexpr int LDS = CG::LDS > CD::LDS ? CG::LDS : CD::LDS;
+    auto kern = moe_experts_kernel<BM, SBG, SBD, WBITS>;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess) return attr;
+    const int tiles_m = (f.gu.M + BM - 1) / BM;
+    const int tiles_n_gu = (f.gu.N / 2 + kBN / 2 - 1) / (kBN / 2);
+    const int tiles_n_dn = (f.dn.N + kBN - 1) / kBN;
+    const int64_t work = (int64_t)f.gu.E * std::max<int64_t>(std::max(tiles_m * tiles_n_gu, tiles_m * tiles_n_dn),
+                                                              (f.gu.M + 7) / 8);
+    if (work <= 0) return hipSuccess;
+    if (work > 0x7fffffff) return hipErrorInvalidValue;
+    int ncu = 0;
+    const hipError_t err = device_cus(&ncu);
+    if (err != hipSuccess) return err;
+    const int grid = (int)(work < ncu ? work : ncu);  // at most one workgroup per CU: all resident together
+    kern<<<dim3((unsigned)grid), dim3(kThreads), LDS, st>>>(f, tiles_n_gu, tiles_n_dn);
+    return hipGetLastError();
+}
+
+template <int WBITS>
+hipError_t launch_fused_bits(const FusedExperts& f, hipStream_t st) {
+    // the ring depths of launch_epi for the two epilogues
+    if constexpr (WBITS == 8) {
+        if (f.gu.M <= 64) return launch_fused_cfg<64, 7, 8, 8>(f, st);
+        if (f.gu.M <= 128) return launch_fused_cfg<128, 6, 7, 8>(f, st);
+        return launch_fused_cfg<256, 5, 6, 8>(f, st);
+    } else {
+        if (f.gu.M <= 64) return launch_fused_cfg<64, 12, 14, 4>(f, st);
+        if (f.gu.M <= 128) return launch_fused_cfg<128, 11, 13, 4>(f, st);
+        return launch_fused_cfg<256, 8, 10, 4>(f, st);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t st) {
@@ -770,6 +966,24 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t st) {
         case Epi::kSwiGLU: return launch_epi<Epi::kSwiGLU, 8, true>(p, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool moe_experts_supported(const GemmProblem& gu, const GemmProblem& dn, int group) {
+    const int I = gu.N / 2;
+    const bool rows_ok = (group == 256 && I == 8 * 256) ||
+                         (group == 64 && I % (8 * 64) == 0 && I / (8 * 64) >= 1 && I / (8 * 64) <= 4);
+    const bool shapes_ok = gu.b_tiled && dn.b_tiled && gu.wbits == dn.wbits && (gu.wbits == 8 || gu.wbits == 4) &&
+                           gu.epi == Epi::kSwiGLU && dn.epi == Epi::kBf16 && dn.E == gu.E && dn.M == gu.M &&
+                           dn.K == I && gu.N % 2 == 0 && dn.a_rows == nullptr && gu.E >= 1 && gu.M >= 1;
+    // an output tile must fit one buffer range (as in launch_cfg)
+    return rows_ok && shapes_ok && (int64_t)256 * I * 2 < kOobOffset && (int64_t)256 * dn.N * 2 < kOobOffset;
+}
+
+hipError_t launch_moe_experts(const GemmProblem& gu, const GemmProblem& dn, const uint16_t* a, int8_t* qa, float* sa,
+                              int group, uint32_t* esync, hipStream_t st) {
+    if (!moe_experts_supported(gu, dn, group) || esync == nullptr) return hipErrorNotSupported;
+    FusedExperts f{gu, dn, a, qa, sa, group, esync};
+    return gu.wbits == 4 ? launch_fused_bits<4>(f, st) : launch_fused_bits<8>(f, st);
 }
 
 }  // namespace crk

@@ -45,9 +45,10 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
 bool select_rotq_supported(int T, int E, int K, int group);
 hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
                               uint64_t* tokmask, const uint16_t* x, int K, int group, int8_t* qx, float* sx,
-                              int64_t row0, hipStream_t st);
+                              int64_t row0, uint32_t* esync, hipStream_t st);
+// esync (nullable): the 2E counters of launch_moe_experts, zeroed by the selection of each expert.
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
-                              int32_t* slotmap, uint64_t* tokmask, hipStream_t st);
+                              int32_t* slotmap, uint64_t* tokmask, uint32_t* esync, hipStream_t st);
 // slotmap [E, T] and the token masks [T, ceil(E / 64)] from idx [E, C].
 hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, uint64_t* tokmask,
                                 hipStream_t st);
@@ -73,6 +74,19 @@ struct GemmProblem {
     Epi epi;
 };
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t st);
+
+// Counters of launch_moe_experts sit kEsyncStride words apart (one 256-byte line each): counter k (gate/up tiles
+// of expert e at k = 2 e, rotate + quantise items at k = 2 e + 1) is esync[k * kEsyncStride].
+constexpr int kEsyncStride = 64;
+
+// The expert part of the MoE layer in one persistent launch: the gate/up GEMM gu (kSwiGLU, writing a), the
+// rotate + quantise of a's rows (rotation group `group`, I = gu.N / 2 columns) into qa / sa, and the down GEMM
+// dn (kBf16, reading qa / sa as its rows e * C + c), with per-expert dependencies through esync (2 gu.E
+// counters kEsyncStride words apart, zero at the start).  hipErrorNotSupported: shape outside the fused kernels, use the three launches.
+hipError_t launch_moe_experts(const GemmProblem& gu, const GemmProblem& dn, const uint16_t* a, int8_t* qa, float* sa,
+                              int group, uint32_t* esync, hipStream_t st);
+// Whether launch_moe_experts takes these problems (host logic only).
+bool moe_experts_supported(const GemmProblem& gu, const GemmProblem& dn, int group);
 
 // ---- combine ------------------------------------------------------------------------------------------
 hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const uint64_t* tokmask, const float* wt, int T,

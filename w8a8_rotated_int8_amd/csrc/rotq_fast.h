@@ -52,23 +52,38 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
     return ab | cd;
 }
 
-// Rounds [part R, part R + R) of one row by this wavefront; WPR wavefronts of the workgroup (consecutive, this
-// one among them) share the row and exchange their maxima through xch (WPR floats from the group's first
-// wavefront on) behind a workgroup barrier, which every wavefront reaches (valid = false: a row past the end,
-// nothing read or written).  WPR = 1: one row per wavefront, no exchange.
+// The bf16 bits of this lane's part of a row: R rounds of E = g / 8 elements, 16 bytes per uint4.
+template <int G, int R>
+struct RotqRaw {
+    uint4 d[R][G / 64];
+};
+
+template <int G, int R>
+__device__ __forceinline__ void rotq_fast_load(const uint16_t* __restrict__ x, int64_t row, bool valid, int K, int part,
+                                               RotqRaw<G, R>& raw) {
+    constexpr int E = G / 8;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* src = x + row * (int64_t)K + (int64_t)part * R * 8 * G + lane * E;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < E / 8; ++c)
+            raw.d[r][c] = valid ? *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Rotate + quantise of a row part already loaded by rotq_fast_load.
 template <int G, int R, int WPR>
-__device__ __forceinline__ void rotq_fast_part(const uint16_t* __restrict__ x, int64_t row, bool valid, int K, int part,
-                                               int8_t* __restrict__ q, float* __restrict__ s, float* xch) {
+__device__ __forceinline__ void rotq_fast_finish(const RotqRaw<G, R>& raw_in, int64_t row, bool valid, int K, int part,
+                                                 int8_t* __restrict__ q, float* __restrict__ s, float* xch) {
     constexpr int E = G / 8;  // elements per lane per round
     const int lane = threadIdx.x & 63;
     const int64_t off0 = row * (int64_t)K + (int64_t)part * R * 8 * G + lane * E;
-    const uint16_t* src = x + off0;
     float v[R][E];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < E / 8; ++c) {
-            const uint4 raw = valid ? *reinterpret_cast<const uint4*>(src + r * 8 * G + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 raw = raw_in.d[r][c];
             const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -159,6 +174,18 @@ __device__ __forceinline__ void rotq_fast_part(const uint16_t* __restrict__ x, i
         }
     }
     if (lane == 0 && part == 0) s[row] = scale;
+}
+
+// Rounds [part R, part R + R) of one row by this wavefront; WPR wavefronts of the workgroup (consecutive, this
+// one among them) share the row and exchange their maxima through xch (WPR floats from the group's first
+// wavefront on) behind a workgroup barrier, which every wavefront reaches (valid = false: a row past the end,
+// nothing read or written).  WPR = 1: one row per wavefront, no exchange.
+template <int G, int R, int WPR>
+__device__ __forceinline__ void rotq_fast_part(const uint16_t* __restrict__ x, int64_t row, bool valid, int K, int part,
+                                               int8_t* __restrict__ q, float* __restrict__ s, float* xch) {
+    RotqRaw<G, R> raw;
+    rotq_fast_load<G, R>(x, row, valid, K, part, raw);
+    rotq_fast_finish<G, R, WPR>(raw, row, valid, K, part, q, s, xch);
 }
 
 // One row per wavefront (row < rows is the caller's check).

@@ -259,12 +259,16 @@ template <int KR>
 __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ probs_t, int T, int C,
                                                     int32_t* __restrict__ idx, float* __restrict__ wt,
                                                     int32_t* __restrict__ slotmap, uint64_t* __restrict__ tokmask,
-                                                    int nw, int e) {
+                                                    int nw, int e, uint32_t* __restrict__ esync) {
     __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
     __shared__ uint32_t s_red[2 * kSelV];
     __shared__ uint32_t s_bcast[2];
     __shared__ int s_cnt[2 * kSelV];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (esync && tid == 0) {  // this expert's counters of the fused expert launch that follows
+        esync[(2 * e) * kEsyncStride] = 0u;
+        esync[(2 * e + 1) * kEsyncStride] = 0u;
+    }
     const float* p = probs_t + (int64_t)e * T;
     const int tb = w * 256 * KR + 4 * lane;  // token of (round j, c): tb + 256 j + c
     const bool vec = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
@@ -455,8 +459,9 @@ template <int KR>
 __global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                    int32_t* __restrict__ idx, float* __restrict__ wt,
                                                                    int32_t* __restrict__ slotmap,
-                                                                   uint64_t* __restrict__ tokmask, int nw) {
-    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x);
+                                                                   uint64_t* __restrict__ tokmask, int nw,
+                                                                   uint32_t* __restrict__ esync) {
+    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x, esync);
 }
 
 // The selection and the rest of the token rotate+quantise in one launch: the first E workgroups select (one
@@ -468,9 +473,9 @@ __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __
                                                                  uint64_t* __restrict__ tokmask, int nw,
                                                                  const uint16_t* __restrict__ x, int K,
                                                                  int8_t* __restrict__ qx, float* __restrict__ sx,
-                                                                 int64_t row0) {
+                                                                 int64_t row0, uint32_t* __restrict__ esync) {
     if ((int)blockIdx.x < E) {  // workgroup-uniform
-        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x);
+        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x, esync);
         return;
     }
     const int64_t row = row0 + (int64_t)(blockIdx.x - E) * kSelV + (threadIdx.x >> 6);
@@ -482,13 +487,18 @@ __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __
 __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
                                                                   int32_t* __restrict__ slotmap,
-                                                                  uint64_t* __restrict__ tokmask, int nw) {
+                                                                  uint64_t* __restrict__ tokmask, int nw,
+                                                                  uint32_t* __restrict__ esync) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_prefix, s_remaining;
     __shared__ int scratch[kSelWaves];
 
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
+    if (esync && tid == 0) {  // this expert's counters of the fused expert launch that follows
+        esync[(2 * e) * kEsyncStride] = 0u;
+        esync[(2 * e + 1) * kEsyncStride] = 0u;
+    }
     const float* p = probs_t + (int64_t)e * T;
 
     uint32_t prefix = 0, mask = 0, remaining = (uint32_t)C;
@@ -623,12 +633,12 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
 }
 
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
-                              int32_t* slotmap, uint64_t* tokmask, hipStream_t st) {
+                              int32_t* slotmap, uint64_t* tokmask, uint32_t* esync, hipStream_t st) {
     const int nw = (E + 63) >> 6;
 #define CRK_SEL(K)                                                                                              \
     if (T <= kSelV * 256 * K) {                                                                                 \
         select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, \
-                                                                      nw);                                      \
+                                                                      nw, esync);                               \
         return hipGetLastError();                                                                               \
     }
     CRK_SEL(1)
@@ -637,7 +647,7 @@ hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t
     CRK_SEL(8)
     CRK_SEL(16)
 #undef CRK_SEL
-    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, nw);
+    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, esync);
     return hipGetLastError();
 }
 
@@ -648,7 +658,7 @@ bool select_rotq_supported(int T, int E, int K, int group) {
 
 hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
                               uint64_t* tokmask, const uint16_t* x, int K, int group, int8_t* qx, float* sx,
-                              int64_t row0, hipStream_t st) {
+                              int64_t row0, uint32_t* esync, hipStream_t st) {
     const int nw = (E + 63) >> 6;
     if (!select_rotq_supported(T, E, K, group) || row0 < 0 || row0 > T) return hipErrorNotSupported;
     const int R = K / (8 * group);
@@ -657,7 +667,7 @@ hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t
 #define CRK_SR2(KK, GG, RR)                                                                                 \
     if (T <= kSelV * 256 * KK && group == GG && R == RR) {                                                  \
         select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slotmap, tokmask, nw, \
-                                                               x, K, qx, sx, row0);                        \
+                                                               x, K, qx, sx, row0, esync);                 \
         return hipGetLastError();                                                                           \
     }
 #define CRK_SR2_G(KK) CRK_SR2(KK, 256, 1) CRK_SR2(KK, 256, 2) CRK_SR2(KK, 256, 4) CRK_SR2(KK, 64, 1) \
