@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kConvThreads) void quantize_g16_kernel(const uint16
 // ---- GEMM + dequant ---------------------------------------------------------------------------------------
 // Workgroup tile 256 tokens x 256 weight rows, 8 wavefronts of 64 tokens x 128 rows (2 x 4 blocks of 32 x 32),
 // K in steps of 64 (four groups).  Each step is staged in LDS already decoded to fp16 (tokens: code; weights:
-// code * f), double-buffered (144 KiB): the next step's global loads are in flight while the current one is
-// multiplied.  The 256 x 256 tile measured 18 % faster than 128 x 128 (half the decode and a third less LDS
+// code * f), double-buffered (144 KiB): the step after the current one is decoded into the other buffer while
+// the current one is multiplied, and the global loads of the step after that are in flight.  The 256 x 256 tile measured 18 % faster than 128 x 128 (half the decode and a third less LDS
 // traffic per multiply-add), and K steps of 64 faster than 32.
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 512;
@@ -180,11 +180,12 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 bits_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 
+// Group u of this thread's token codes, decoded, into the stage's token rows.
 template <int BITS>
-__device__ __forceinline__ void stage_store_group(const StageRegs<BITS>& r, int u, _Float16* As, _Float16* Bs) {
+__device__ __forceinline__ void stage_store_tokens(const StageRegs<BITS>& r, int u, _Float16* As) {
     const int t = threadIdx.x, row = t >> 1, hk = t & 1;
-    uint32_t a[8], b[8];
-    // tokens: bytes k and k + 4 of each 8-byte chunk into one register, sign bit flipped (x + 128 in 0..255)
+    uint32_t a[8];
+    // bytes k and k + 4 of each 8-byte chunk into one register, sign bit flipped (x + 128 in 0..255)
     const uint32_t aw[4] = {r.a[u].x, r.a[u].y, r.a[u].z, r.a[u].w};
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -193,6 +194,16 @@ __device__ __forceinline__ void stage_store_group(const StageRegs<BITS>& r, int 
             const uint32_t x = __builtin_amdgcn_perm(aw[2 * c + 1], aw[2 * c], 0x0c040c00u + (uint32_t)(i | (i << 16)));
             a[4 * c + i] = h2_bits(bits_h2(x ^ 0x64806480u) - h2{(_Float16)1152.0f, (_Float16)1152.0f});
         }
+    uint32_t* ao = reinterpret_cast<uint32_t*>(As + row * kRowHalves + 16 * (kGPT * hk + u));
+    *reinterpret_cast<uint4*>(ao) = make_uint4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<uint4*>(ao + 4) = make_uint4(a[4], a[5], a[6], a[7]);
+}
+
+// Group u of this thread's weight codes, decoded and scaled by the group's E4M3 factor, into the weight rows.
+template <int BITS>
+__device__ __forceinline__ void stage_store_weights(const StageRegs<BITS>& r, int u, _Float16* Bs) {
+    const int t = threadIdx.x, row = t >> 1, hk = t & 1;
+    uint32_t b[8];
     const _Float16 fh = (_Float16)e4m3_decode(r.f[u]);  // every E4M3 value is an fp16 value
     const h2 f2{fh, fh};
     if constexpr (BITS == 4) {
@@ -221,18 +232,24 @@ __device__ __forceinline__ void stage_store_group(const StageRegs<BITS>& r, int 
                     h2_bits((bits_h2(x ^ 0x64206420u) - h2{(_Float16)1056.0f, (_Float16)1056.0f}) * f2);
             }
     }
-    uint32_t* ao = reinterpret_cast<uint32_t*>(As + row * kRowHalves + 16 * (kGPT * hk + u));
     uint32_t* bo = reinterpret_cast<uint32_t*>(Bs + row * kRowHalves + 16 * (kGPT * hk + u));
-    *reinterpret_cast<uint4*>(ao) = make_uint4(a[0], a[1], a[2], a[3]);
-    *reinterpret_cast<uint4*>(ao + 4) = make_uint4(a[4], a[5], a[6], a[7]);
     *reinterpret_cast<uint4*>(bo) = make_uint4(b[0], b[1], b[2], b[3]);
     *reinterpret_cast<uint4*>(bo + 4) = make_uint4(b[4], b[5], b[6], b[7]);
+}
+
+// Part p (0..3) of a stage's decode: tokens or weights (p % 2) of group p / 2.
+template <int BITS>
+__device__ __forceinline__ void stage_store_part(const StageRegs<BITS>& r, int p, _Float16* As, _Float16* Bs) {
+    if (p & 1)
+        stage_store_weights<BITS>(r, p >> 1, Bs);
+    else
+        stage_store_tokens<BITS>(r, p >> 1, As);
 }
 
 template <int BITS>
 __device__ __forceinline__ void stage_store(const StageRegs<BITS>& r, _Float16* As, _Float16* Bs) {
 #pragma unroll
-    for (int u = 0; u < kGPT; ++u) stage_store_group<BITS>(r, u, As, Bs);
+    for (int p = 0; p < 2 * kGPT; ++p) stage_store_part<BITS>(r, p, As, Bs);
 }
 
 template <int BITS>
@@ -260,32 +277,56 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_g16_kernel(const int8_t* __
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    StageRegs<BITS> regs;
-    stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, 0);
-    stage_store<BITS>(regs, Abuf(0), Bbuf(0));
+    // Stage kt is multiplied from LDS buffer kt % 2 while stage kt + 1, loaded into registers one step earlier,
+    // is decoded into the other buffer, one quarter per 16-deep slice, so the decode's VALU work runs beside the
+    // matrix work; the global loads of stage kt + 2 go to the second register set.  One barrier per step.
+    StageRegs<BITS> ra, rb;
+    stage_load<BITS>(ra, qx, M, K, qw, f8, N, m0, n0, 0);
+    stage_store<BITS>(ra, Abuf(0), Bbuf(0));
+    if (nk > 1) stage_load<BITS>(ra, qx, M, K, qw, f8, N, m0, n0, kBK);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
+    // fragments of slice sl (16 deep): row lane % 32 of a 32-row block, halves 16 sl + 8 (lane / 32) .. + 8
+    auto read_frags = [&](int buf, int sl, v8h (&af)[2], v8h (&bf)[kWN]) {
+        const int col = 16 * sl + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            af[i] = *reinterpret_cast<const v8h*>(Abuf(buf) + (wm * 64 + 32 * i + (lane & 31)) * kRowHalves + col);
+#pragma unroll
+        for (int j = 0; j < kWN; ++j)
+            bf[j] = *reinterpret_cast<const v8h*>(Bbuf(buf) + (wn * 128 + 32 * j + (lane & 31)) * kRowHalves + col);
+    };
+    auto step = [&](int kt, const StageRegs<BITS>& dec, StageRegs<BITS>& ld) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) stage_load<BITS>(regs, qx, M, K, qw, f8, N, m0, n0, (kt + 1) * kBK);
+        if (kt + 2 < nk) stage_load<BITS>(ld, qx, M, K, qw, f8, N, m0, n0, (kt + 2) * kBK);
+        // the next slice's fragments are read while the current slice multiplies
+        v8h af[2][2], bf[2][kWN];
+        read_frags(buf, 0, af[0], bf[0]);
 #pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            // fragment: row lane % 32 of a 32-row block, halves 16 s + 8 (lane / 32) .. + 8
-            const int col = 16 * s + 8 * (lane >> 5);
-            v8h af[2], bf[kWN];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const v8h*>(Abuf(buf) + (wm * 64 + 32 * i + (lane & 31)) * kRowHalves + col);
-#pragma unroll
-            for (int j = 0; j < kWN; ++j)
-                bf[j] = *reinterpret_cast<const v8h*>(Bbuf(buf) + (wn * 128 + 32 * j + (lane & 31)) * kRowHalves + col);
+        for (int sl = 0; sl < kBK / 16; ++sl) {
+            if (sl + 1 < kBK / 16) read_frags(buf, sl + 1, af[(sl + 1) & 1], bf[(sl + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < kWN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[sl & 1][j], af[sl & 1][i], acc[i][j], 0, 0, 0);
+            // unconditional, to keep one scheduling region: on the last step it decodes stale registers into the
+            // buffer no one reads any more (every read of it ended at the previous barrier)
+            stage_store_part<BITS>(dec, sl, Abuf(buf ^ 1), Bbuf(buf ^ 1));
+            // issue order: the next slice's fragment reads, then each MFMA followed by a few of the decode's
+            // VALU instructions (they run while the MFMA does), then the decode's LDS stores
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 + kWN, 0);
+#pragma unroll
+            for (int m = 0; m < 2 * kWN; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
         }
-        if (kt + 1 < nk) stage_store<BITS>(regs, Abuf(buf ^ 1), Bbuf(buf ^ 1));
         __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, ra, rb);
+        if (kt + 1 < nk) step(kt + 1, rb, ra);
     }
 
     // The weights are the MFMA's first operand: lane l holds token l % 32 of each 32 x 32 block and, in
