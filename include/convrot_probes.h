@@ -27,8 +27,8 @@ extern "C" {
 size_t convrot_probe_out_words(void);
 
 /* int8 MFMA rate on changing operands.  Every wavefront loads 8 operand registers from src (device, at least
- * 256 KiB, read cyclically) and runs iters rounds of 16 v_mfma_i32_32x32x32_i8 over 4 independent
- * accumulators, each MFMA taking a different operand pair from the one before (the MFMA's power, and with it
+ * 256 KiB, read cyclically) and runs iters rounds of 32 v_mfma_i32_16x16x64_i8 (the grouped GEMMs'
+ * instruction) over 8 independent accumulators, each MFMA taking a different operand pair from the one before (the MFMA's power, and with it
  * the clock the chip holds, depends on the bits it multiplies: random bytes give the rate a GEMM on random
  * data can reach).  out (device, convrot_probe_out_words() words) receives the accumulators' xor per thread.
  * *ops (host) = the int8 operations the launch performs (2 per multiply-add). */

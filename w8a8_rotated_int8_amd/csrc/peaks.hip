@@ -11,7 +11,6 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 8;
@@ -39,21 +38,21 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const v4i* __restri
         a[j] = src[((w * 8 + j) * 64 + lane) % kVec];
         b[j] = src[((w * 8 + 4 + j) * 64 + lane) % kVec];
     }
-    v16i acc[4];
+    v4i acc[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < 8; ++j) acc[j] = v4i{0, 0, 0, 0};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[(j + r) & 3], b[j], acc[j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j)
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[(j + r) & 3], b[j & 3], acc[j], 0, 0, 0);
     }
     int x = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int k = 0; k < 16; ++k) x ^= acc[j][k];
+        for (int k = 0; k < 4; ++k) x ^= acc[j][k];
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = x;
 }
 
@@ -99,7 +98,7 @@ convrot_status convrot_probe_mfma_i8(const int8_t* src, size_t src_bytes, int it
     mfma_rate_kernel<<<dim3((unsigned)ncu), dim3(kThreads), 0, stream>>>(reinterpret_cast<const v4i*>(src), iters,
                                                                           out);
     if (hipGetLastError() != hipSuccess) return CONVROT_ERR_HIP;
-    *ops = (double)ncu * kWaves * iters * 16 * (2.0 * 32 * 32 * 32);
+    *ops = (double)ncu * kWaves * iters * 32 * (2.0 * 16 * 16 * 64);
     return CONVROT_OK;
 }
 
