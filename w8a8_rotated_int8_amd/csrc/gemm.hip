@@ -868,8 +868,8 @@ __global__ __launch_bounds__(kThreads, 2) void moe_experts_kernel(const FusedExp
 
     // phase 2: rotate + quantise of the hidden rows, after every gate/up tile of the experts of this workgroup's
     // items; wavefront w takes row 8 (item % nrb) + w of each item, with the loads of up to kRowsInFlight rows
-    // issued before any of them is transformed (one wavefront per SIMD pair would otherwise wait a full
-    // memory latency per row)
+    // issued before any of them is transformed (with only 8 wavefronts per CU, each would otherwise wait a
+    // full memory latency per row)
     const int nrb = (C + 7) / 8;
     const XcdSplit s2(E * nrb, G, wg);
     if (threadIdx.x == 0) {
@@ -928,7 +928,8 @@ hipError_t launch_fused_cfg(const FusedExperts& f, hipStream_t st) {
     int ncu = 0;
     const hipError_t err = device_cus(&ncu);
     if (err != hipSuccess) return err;
-    const int grid = (int)(work < ncu ? work : ncu);  // at most one workgroup per CU: all resident together
+    // no more workgroups than CUs, and each fits a CU on its own: all are resident together on an idle device
+    const int grid = (int)(work < ncu ? work : ncu);
     kern<<<dim3((unsigned)grid), dim3(kThreads), LDS, st>>>(f, tiles_n_gu, tiles_n_dn);
     return hipGetLastError();
 }
