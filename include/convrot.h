@@ -193,8 +193,10 @@ convrot_status moe_expert_choice_forward(const uint16_t* x, int T, const float* 
  * (a row's scale needs all of its I columns, which come from several CUs, so the quantisation cannot sit in
  * the gate/up epilogue itself).  It needs every one of its workgroups resident at once: a kernel of another
  * stream that holds CUs delays it, and one holding them for more than about a second per wait leaves wrong
- * results (the waits are bounded; the launch always finishes).  On MI355X it is slower than the three
- * launches of moe_expert_choice_forward, whose kernel boundaries cost next to nothing.
+ * results (the waits are bounded; the launch always finishes).  Two of these calls must not run concurrently
+ * on one GPU (from two streams): each could hold CUs that the other's waiting workgroups need.  On MI355X it
+ * is slower than the three launches of moe_expert_choice_forward, whose kernel boundaries cost next to
+ * nothing.
  * CONVROT_ERR_SHAPE where moe_expert_choice_fused(w, C) is 0; other errors as moe_expert_choice_forward. */
 convrot_status moe_expert_choice_forward_fused(const uint16_t* x, int T, const float* router_logits, int C,
                                                const convrot_moe_weights* w, uint16_t* out, int32_t* idx_out,
