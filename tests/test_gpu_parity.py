@@ -401,6 +401,15 @@ def test_single_expert_ffn_config1():
     assert exact == 1.0
 
 
+def test_moe_forward_fused_without_routing_outputs():
+    shape = FUSED[0]
+    say(f"moe forward, one expert launch, NULL routing outputs {shape}")
+    x, lg, w, ref = _layer(shape, 8, 30100)
+    out, idx, wt = cr.moe_expert_choice_forward(dev_bf16(x), dev(lg), shape.C, w, want_routing=False, fused=True)
+    assert idx is None and wt is None
+    assert np.array_equal(host_bf16(out), ref["out"]), "moe out"
+
+
 def test_moe_forward_fused_rejects_other_shapes():
     shape = SMALL[0]  # I = 128: rows too short for the one-launch path
     x, lg, w_gu, w_dn = synth.moe_inputs(2, shape, seed_base=40000)
