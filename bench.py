@@ -59,7 +59,9 @@ def gateup_ops(s) -> float:
 
 
 def src_hash(path) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """The GEMM source's code digest, as the counter summaries record it (comments do not count)."""
+    from w8a8_rotated_int8_amd.profiling import gemm_code_digest
+    return gemm_code_digest(path)
 
 
 def read_traffic():
@@ -68,7 +70,7 @@ def read_traffic():
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
-    m = re.search(r"gemm_source_sha256_16:\s*(\w+)", text)
+    m = re.search(r"gemm_code_sha256_16:\s*(\w+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != src_hash(GEMM_SRC):
         return None

@@ -24,6 +24,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SRC = os.path.join(ROOT, "w8a8_rotated_int8_amd", "csrc", "gemm.hip")
 
 
+def gemm_code_digest(path: str = GEMM_SRC) -> str:
+    """First 16 hex digits of the SHA-256 of the GEMM source's code: every line with its // comment, trailing
+    blanks and blank lines dropped, so that a change of comments alone keeps the committed counter summaries
+    valid while any change of code invalidates them."""
+    lines = []
+    for line in open(path, encoding="utf-8").read().splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def _csv(run_dir: str, suffix: str):
     path = os.path.join(run_dir, f"run_{suffix}.csv")
     if not os.path.exists(path):
@@ -133,8 +145,7 @@ def pmc_summary(out_txt: str, command: str, kernels: str, run_dirs) -> None:
     seen by the vector caches."""
     lines = [f"command: {command}", "source: rocprofv3 --pmc (counter_collection.csv), one pass per counter set;",
              "  values are means per dispatch after the first; the profiler serialises dispatches, so the clock",
-             "  here is the unthrottled one", f"gemm_source_sha256_16: "
-             f"{hashlib.sha256(open(GEMM_SRC, 'rb').read()).hexdigest()[:16]}", ""]
+             "  here is the unthrottled one", f"gemm_code_sha256_16: {gemm_code_digest()}", ""]
     for spec in kernels.split(","):
         label, pattern = spec.split("=", 1)
         lines.append(f"== {label} (kernel name contains {pattern!r})")
@@ -192,10 +203,10 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_m
     kw, nw = counter_per_dispatch(write_dir, "WRITE_SIZE", pattern)
     fetch_b = kf * 1024.0 * f_scale
     write_b = kw * 1024.0 * w_scale
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    sha = gemm_code_digest()
     lines = [f"command: {command}",
              f"kernel: dispatches whose name contains {pattern!r} ({nf} FETCH, {nw} WRITE dispatches after warm-up)",
-             f"gemm_source_sha256_16: {sha}",
+             f"gemm_code_sha256_16: {sha}",
              f"copy calibration: {copy_mib} MiB device copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB",
              f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}",
              f"fetch_kib_raw: {kf:.1f}", f"write_kib_raw: {kw:.1f}",
