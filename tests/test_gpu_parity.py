@@ -277,6 +277,53 @@ def test_route_from_probs_with_heavy_ties():
         assert np.array_equal(host(wt).view(np.uint32), rwt.view(np.uint32))
 
 
+@pytest.mark.parametrize("n_bin,tie", [(1, False), (7, True), (64, False), (64, True), (65, False), (65, True),
+                                       (300, True)])
+def test_route_few_keys_left_after_first_pass(n_bin, tie):
+    """After the first 11-bit radix pass the threshold's bin holds n_bin keys (0.5 (1 + k 2^-20): same exponent and
+    top mantissa bits, apart from the 0.9 above and the [1e-3, 2e-3) below).  Up to 64 such keys are ranked by one
+    wavefront, more take the further passes; both must give the oracle's list, equal keys in the bin included."""
+    say(f"route few keys left n_bin={n_bin} tie={tie}")
+    rng = np.random.default_rng(100 + n_bin + tie)
+    T, E, n_top = 4096, 2, 37
+    p = np.empty((T, E), np.float32)
+    k = np.arange(n_bin) // (2 if tie else 1)
+    cluster = (np.float32(0.5) * (np.float32(1) + k.astype(np.float32) * np.float32(2.0 ** -20))).astype(np.float32)
+    for e in range(E):
+        col = ((rng.random(T) + 1.0) * 1e-3).astype(np.float32)
+        perm = rng.permutation(T)
+        col[perm[:n_top]] = np.float32(0.9)
+        col[perm[n_top:n_top + n_bin]] = cluster
+        p[:, e] = col
+    for r in sorted({1, n_bin // 2 + 1, n_bin}):
+        C = n_top + r
+        idx, wt, _ = cr.moe_route_expert_choice(dev(p), C, is_probs=True)
+        ridx, rwt = oracle.route_from_probs(p, C)
+        assert np.array_equal(host(idx), ridx), f"C={C}"
+        assert np.array_equal(host(wt).view(np.uint32), rwt.view(np.uint32)), f"C={C}"
+
+
+@pytest.mark.parametrize("mix", [(1, 1, 1, 1, 1, 1, 1), (48, 48, 4, 0, 0, 0, 0)])
+def test_route_from_probs_with_zero_ties_long(mix):
+    """T > 16384: the selection keeps only keys and recovers a selected token's weight from its key, with one
+    bit per key for the sign of zero.  Selected +0 and -0 must come back as they were, for C below the LDS
+    staging limit (1024) and above it."""
+    say(f"route from probs with zero ties, T=20000, mix={mix}")
+    rng = np.random.default_rng(sum(mix))
+    T, E = 20000, 4
+    vals = np.float32([0.0, -0.0, 0.25, 0.5, 0.125, 1e-30, 3e-41])
+    w = np.float64(mix) / np.sum(mix)
+    p = rng.choice(vals, size=(T, E), p=w).astype(np.float32)
+    for C in (3, 1000, 5000, 19999):
+        idx, wt, _ = cr.moe_route_expert_choice(dev(p), C, is_probs=True)
+        ridx, rwt = oracle.route_from_probs(p, C)
+        assert np.array_equal(host(idx), ridx), f"C={C}"
+        assert np.array_equal(host(wt).view(np.uint32), rwt.view(np.uint32)), f"C={C}"
+        sel = rwt.view(np.uint32)
+        if C == 1000 and mix[0] == 48:
+            assert np.any(sel == 0x80000000) and np.any(sel == 0), "both signs of zero selected"
+
+
 # ----------------------------------------------------------------------------------------------------------
 # MoE stages given identical inputs, and the whole layer
 # ----------------------------------------------------------------------------------------------------------

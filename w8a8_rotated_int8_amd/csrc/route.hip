@@ -7,10 +7,11 @@
 //                exponentials and the divisions, one lane keeps the sequential sum, and the probabilities
 //                leave through a transposed LDS tile as 16-byte row stores.
 //  select_topc   one workgroup per expert: radix select (passes of up to 11 bits, most significant first,
-//                after the bits every key shares) of the C-th largest key over keys held in registers, then
-//                one ordered compaction that keeps every token above the threshold and the lowest-index
-//                tokens equal to it.  The list comes out in ascending token order without a sort; ties go
-//                to the lower token index by construction.
+//                after the bits every key shares) of the C-th largest key over keys held in registers; once
+//                at most 64 keys share the decided bits, one wavefront ranks those keys instead of further
+//                passes.  Then one ordered compaction keeps every token above the threshold and the
+//                lowest-index tokens equal to it.  The list comes out in ascending token order without a sort;
+//                ties go to the lower token index by construction.
 //  build_slotmap per expert: slotmap[e, t] = position of t in expert e's list, or -1.
 //  Token masks: where asked for, bit e % 64 of word t * ceil(E / 64) + e / 64 is set when expert e takes token
 //  t (OR is order-independent, so the mask does not depend on which workgroup sets its bit first).  The softmax
@@ -36,13 +37,23 @@ constexpr int kSmTok = 32;
 constexpr int kSmStride = 65;           // LDS row stride of the [token][expert] tile (floats)
 constexpr int kSmTrStride = kSmTok + 1;  // LDS row stride of the [expert][token] tile
 
-// Tokens [32 b, 32 b + 32) (one 256-thread workgroup).
-__device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int is_probs, int T, int E,
+// LDS of one softmax tile, declared once per kernel (both instantiations below share it).
+struct SoftmaxLds {
+    float tile[kSmTok * kSmStride];  // logits, then exponentials
+    float tr[64 * kSmTrStride];      // probabilities, transposed
+    float zrow[kSmTok];
+};
+
+// Tokens [32 b, 32 b + 32) (one 256-thread workgroup).  EF > 0 fixes E = EF at compile time (the router's
+// 64 experts), which removes every per-expert bound check.
+template <int EF>
+__device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int is_probs, int T, int E_arg,
                                              float* __restrict__ probs_t, float* __restrict__ probs_out,
-                                             uint64_t* __restrict__ tokmask, int b) {
-    __shared__ float tile[kSmTok * kSmStride];  // logits, then exponentials
-    __shared__ float tr[64 * kSmTrStride];      // probabilities, transposed
-    __shared__ float zrow[kSmTok];
+                                             uint64_t* __restrict__ tokmask, int b, SoftmaxLds& lds) {
+    const int E = EF > 0 ? EF : E_arg;
+    float* const tile = lds.tile;
+    float* const tr = lds.tr;
+    float* const zrow = lds.zrow;
     const int t0 = b * kSmTok;
     const int ntok = (T - t0) < kSmTok ? (T - t0) : kSmTok;
     const int tid = threadIdx.x, tok = tid >> 3, eg = tid & 7;
@@ -86,10 +97,21 @@ __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int i
         }
         __syncthreads();
         if (eg == 0 && tv) {
+            // the entries are read 16 at a time, one chunk ahead of the sum; an expert past E adds +0, which
+            // leaves the sum of non-negative terms unchanged
+            float ex[2][16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ex[0][i] = row[i];
             float z = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 64; ++e)
-                if (e < E) z = z + row[e];  // ascending expert order
+            for (int ch = 0; ch < 4; ++ch) {
+                if (ch + 1 < 4) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) ex[(ch + 1) & 1][i] = row[16 * (ch + 1) + i];
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) z = z + (16 * ch + i < E ? ex[ch & 1][i] : 0.0f);  // ascending order
+            }
             zrow[tok] = z;
         }
         __syncthreads();
@@ -128,7 +150,11 @@ __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int i
 __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
                                                               float* __restrict__ probs_t, float* __restrict__ probs_out,
                                                               uint64_t* __restrict__ tokmask) {
-    softmax_tile(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x);
+    __shared__ SoftmaxLds lds;
+    if (E == 64)
+        softmax_tile<64>(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x, lds);
+    else
+        softmax_tile<0>(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x, lds);
 }
 
 // The router softmax and token rotate+quantise in one launch: they do not depend on each other, so the first
@@ -140,8 +166,12 @@ __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restri
                                                            int nsm, const uint16_t* __restrict__ x, int K,
                                                            int8_t* __restrict__ qx, float* __restrict__ sx,
                                                            int64_t rows) {
+    __shared__ SoftmaxLds lds;
     if ((int)blockIdx.x < nsm) {  // workgroup-uniform
-        softmax_tile(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x);
+        if (E == 64)
+            softmax_tile<64>(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x, lds);
+        else
+            softmax_tile<0>(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x, lds);
         return;
     }
     const int64_t row = (int64_t)(blockIdx.x - nsm) * 4 + (threadIdx.x >> 6);
@@ -212,6 +242,8 @@ __device__ __forceinline__ int block_excl_sum(int v, int* scratch, int& total) {
 // (# greater keys before it) + min(# equal keys before it, C - # greater keys overall), and both prefixes come
 // from ballots within a round.
 constexpr int kSelV = 8;  // wavefronts per workgroup
+constexpr int kSelFew = 64;     // at most this many keys left in the threshold's bin: one wavefront ranks them
+constexpr int kSelStageC = 1024;  // C up to this: the selected tokens are staged in LDS (in the bins' space)
 constexpr int kSelBins = 2048;  // radix bins of one pass (11 bits)
 // the bins are cleared with one 16-byte chunk per thread of the workgroup
 static_assert(kSelV * 64 * 4 == kSelBins, "selection workgroup size and bin count are tied");
@@ -262,8 +294,11 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
                                                     int nw, int e, uint32_t* __restrict__ esync) {
     __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
     __shared__ uint32_t s_red[2 * kSelV];
-    __shared__ uint32_t s_bcast[2];
+    __shared__ uint32_t s_bcast[3];
     __shared__ int s_cnt[2 * kSelV];
+    __shared__ uint32_t s_cand[kSelFew];
+    __shared__ uint32_t s_ncand;
+    static_assert(2 * kSelStageC <= kSelBins, "staged selection fits the bins");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (esync && tid == 0) {  // this expert's counters of the fused expert launch that follows
         esync[(2 * e) * kEsyncStride] = 0u;
@@ -273,11 +308,12 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
     const int tb = w * 256 * KR + 4 * lane;  // token of (round j, c): tb + 256 j + c
     const bool vec = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
     // Up to 8 rounds the values stay in registers for the weights of the selected tokens; beyond that a
-    // selected token's value comes back from its key (invertible apart from the sign of zero, so a selected
-    // zero is read again).
+    // selected token's value comes back from its key, which is invertible apart from the sign of zero: one bit
+    // per key records a negative zero (bit 4 j + c of word (4 j + c) / 32).
     constexpr bool kKeepVal = KR <= 8;
     uint32_t key[KR][4];
     float val[kKeepVal ? KR : 1][4];
+    uint32_t negz[kKeepVal ? 1 : (4 * KR + 31) / 32] = {};
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
         const int t = tb + 256 * j;
@@ -295,7 +331,10 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             key[j][c] = orderable(f[c]);
-            if constexpr (kKeepVal) val[j][c] = f[c];
+            if constexpr (kKeepVal)
+                val[j][c] = f[c];
+            else
+                negz[(4 * j + c) >> 5] |= (__float_as_uint(f[c]) == 0x80000000u ? 1u : 0u) << ((4 * j + c) & 31);
         }
     }
     // Tokens past T hold key 0, the smallest key there is: they only add to the lowest bins, never exceed the
@@ -326,7 +365,41 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
     const int common = diff ? __clz(diff) : 32;
     uint32_t mask = common ? (0xffffffffu << (32 - common)) : 0u;
     uint32_t prefix = kmin & mask, remaining = (uint32_t)C;
+    uint32_t n_left = kSelV * 256 * KR;  // keys that share the decided bits (the padding past T included)
     for (int hi = 32 - common; hi > 0;) {  // bits [0, hi) still undecided
+        if (n_left <= (uint32_t)kSelFew) {  // workgroup-uniform
+            // Few keys left: gather them, and one wavefront finds the remaining-th largest among them by
+            // counting, for each, the keys above and equal to it.  Every key is compared in full, so the
+            // threshold and the number of equal keys to take are those the remaining passes would give.
+#pragma unroll
+            for (int j = 0; j < KR; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((key[j][c] & mask) == prefix) s_cand[atomicAdd(&s_ncand, 1u)] = key[j][c];
+            __syncthreads();
+            if (w == 0) {
+                const int n = (int)n_left;
+                const uint32_t ck = lane < n ? s_cand[lane] : 0u;
+                uint32_t gt = 0u, eq = 0u;
+                for (int j = 0; j < n; ++j) {
+                    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+                    gt += kj > ck ? 1u : 0u;
+                    eq += kj == ck ? 1u : 0u;
+                }
+                // the candidates in descending order: the remaining-th one has fewer than `remaining` keys
+                // above it and at least `remaining` at or above it (1 <= remaining <= n, so one lane does)
+                const bool hit = lane < n && gt < remaining && remaining <= gt + eq;
+                const int first = __ffsll((unsigned long long)__ballot(hit)) - 1;
+                if (lane == first) {
+                    s_bcast[0] = ck;
+                    s_bcast[1] = remaining - gt;
+                }
+            }
+            __syncthreads();
+            prefix = s_bcast[0];
+            remaining = s_bcast[1];
+            break;
+        }
         const int width = hi < 11 ? hi : 11;
         const int shift = hi - width;
         const uint32_t dmask = (1u << width) - 1u;
@@ -371,11 +444,14 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
                 const int digit = 2047 - 32 * lane - nb;
                 s_bcast[0] = prefix | ((uint32_t)digit << shift);
                 s_bcast[1] = remaining - above;
+                s_bcast[2] = hist[digit];  // keys that share the digit too
+                s_ncand = 0u;
             }
         }
         __syncthreads();
         prefix = s_bcast[0];
         remaining = s_bcast[1];
+        n_left = s_bcast[2];
         mask |= dmask << shift;
     }
     const uint32_t v = prefix;        // the C-th largest key
@@ -405,6 +481,11 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
     }
     int32_t* sm = slotmap ? slotmap + (int64_t)e * T : nullptr;
     const bool vec_sm = vec && sm && (reinterpret_cast<uintptr_t>(sm) & 15) == 0;
+    // C <= kSelStageC: the selected tokens and weights go to LDS by slot (the bins are free: the last read of
+    // them was before the last barrier), and leave in slot order once all are placed
+    const bool stage = C <= kSelStageC;  // workgroup-uniform
+    int32_t* const s_tok = reinterpret_cast<int32_t*>(hist);
+    float* const s_w = reinterpret_cast<float*>(hist + kSelStageC);
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
         const int t = tb + 256 * j;
@@ -427,16 +508,22 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
             const int pos = gtr + (eqr < need_eq ? eqr : need_eq);
             slot[c] = sel ? pos : -1;
             if (sel && pos < C) {
-                idx[(int64_t)e * C + pos] = t + c;
-                if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
                 float v_out;
                 if constexpr (kKeepVal) {
                     v_out = val[j][c];
                 } else {
                     const uint32_t k = key[j][c];
-                    v_out = k == 0x80000000u ? p[t + c] : __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+                    const uint32_t zbit = (negz[(4 * j + c) >> 5] >> ((4 * j + c) & 31)) & 1u;
+                    v_out = __uint_as_float((k & 0x80000000u) ? ((k & 0x7fffffffu) | (zbit << 31)) : ~k);
                 }
-                wt[(int64_t)e * C + pos] = v_out;
+                if (stage) {
+                    s_tok[pos] = t + c;
+                    s_w[pos] = v_out;
+                } else {
+                    idx[(int64_t)e * C + pos] = t + c;
+                    if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
+                    wt[(int64_t)e * C + pos] = v_out;
+                }
             }
             eqr += eq[c] ? 1 : 0;
             gtr += gt[c] ? 1 : 0;
@@ -452,6 +539,15 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
         }
         eqb += tot_eq;
         gtb += tot_gt;
+    }
+    if (stage) {
+        __syncthreads();
+        for (int i = tid; i < C; i += kSelV * 64) {  // every slot below C holds one selected token (C <= T)
+            const int tt = s_tok[i];
+            idx[(int64_t)e * C + i] = tt;
+            wt[(int64_t)e * C + i] = s_w[i];
+            if (tokmask) atomicOr(tokmask + (int64_t)tt * nw + (e >> 6), 1ull << (e & 63));
+        }
     }
 }
 
