@@ -12,10 +12,14 @@
 //                passes.  Then one ordered compaction keeps every token above the threshold and the
 //                lowest-index tokens equal to it.  The list comes out in ascending token order without a sort;
 //                ties go to the lower token index by construction.
-//  build_slotmap per expert: slotmap[e, t] = position of t in expert e's list, or -1.
+//  Slot map: slotmap[e, t] = position of t in expert e's list.  The selections write only the entries of the
+//                tokens they take, at the same time as the token mask bit; the combine reads an entry only
+//                where that bit is set (build_slotmap, for the stand-alone combine, writes -1 everywhere else).
 //  Token masks: where asked for, bit e % 64 of word t * ceil(E / 64) + e / 64 is set when expert e takes token
 //  t (OR is order-independent, so the mask does not depend on which workgroup sets its bit first).  The softmax
 //  launch, which runs before the selection, clears the words of its tokens.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "rotq_fast.h"
@@ -243,7 +247,7 @@ __device__ __forceinline__ int block_excl_sum(int v, int* scratch, int& total) {
 // from ballots within a round.
 constexpr int kSelV = 8;  // wavefronts per workgroup
 constexpr int kSelFew = 64;     // at most this many keys left in the threshold's bin: one wavefront ranks them
-constexpr int kSelStageC = 1024;  // C up to this: the selected tokens are staged in LDS (in the bins' space)
+constexpr int kSelStageC = 960;  // C up to this: the selected tokens are staged in LDS (in the bins' space)
 constexpr int kSelBins = 2048;  // radix bins of one pass (11 bits)
 // the bins are cleared with one 16-byte chunk per thread of the workgroup
 static_assert(kSelV * 64 * 4 == kSelBins, "selection workgroup size and bin count are tied");
@@ -298,7 +302,9 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
     __shared__ int s_cnt[2 * kSelV];
     __shared__ uint32_t s_cand[kSelFew];
     __shared__ uint32_t s_ncand;
-    static_assert(2 * kSelStageC <= kSelBins, "staged selection fits the bins");
+    // staged tokens at hist[slot], weights at hist[1024 + slot]; slots kSelStageC + lane take the writes of
+    // lanes that select nothing
+    static_assert(kSelStageC + 64 <= kSelBins / 2, "staged selection fits the bins");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (esync && tid == 0) {  // this expert's counters of the fused expert launch that follows
         esync[(2 * e) * kEsyncStride] = 0u;
@@ -480,65 +486,81 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
         gtb += x < w ? s_cnt[kSelV + x] : 0;
     }
     int32_t* sm = slotmap ? slotmap + (int64_t)e * T : nullptr;
-    const bool vec_sm = vec && sm && (reinterpret_cast<uintptr_t>(sm) & 15) == 0;
     // C <= kSelStageC: the selected tokens and weights go to LDS by slot (the bins are free: the last read of
-    // them was before the last barrier), and leave in slot order once all are placed
-    const bool stage = C <= kSelStageC;  // workgroup-uniform
+    // them was before the last barrier), and leave in slot order once all are placed.  Up to 8 rounds the rounds
+    // are compiled once per choice (workgroup-uniform), so neither path carries the other's branches; more
+    // rounds keep one copy that decides per token (two copies of 16 rounds would spill).
+    const bool stage = C <= kSelStageC;
     int32_t* const s_tok = reinterpret_cast<int32_t*>(hist);
-    float* const s_w = reinterpret_cast<float*>(hist + kSelStageC);
+    float* const s_w = reinterpret_cast<float*>(hist + kSelBins / 2);
+    // mode 0: direct stores, 1: staged, 2: decided per token by `stage`
+    auto rounds = [&](auto mode_c) {
+        constexpr int kMode = decltype(mode_c)::value;
 #pragma unroll
-    for (int j = 0; j < KR; ++j) {
-        const int t = tb + 256 * j;
-        bool eq[4], gt[4];
-        int ne = 0, ng = 0;
+        for (int j = 0; j < KR; ++j) {
+            const int t = tb + 256 * j;
+            bool eq[4], gt[4];
+            int ne = 0, ng = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            eq[c] = key[j][c] == v;
-            gt[c] = key[j][c] > v;
-            ne += eq[c] ? 1 : 0;
-            ng += gt[c] ? 1 : 0;
-        }
-        int tot_eq, tot_gt;
-        int eqr = eqb + lanes_below(ne, tot_eq);
-        int gtr = gtb + lanes_below(ng, tot_gt);
-        int slot[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bool sel = gt[c] || (eq[c] && eqr < need_eq);
-            const int pos = gtr + (eqr < need_eq ? eqr : need_eq);
-            slot[c] = sel ? pos : -1;
-            if (sel && pos < C) {
-                float v_out;
-                if constexpr (kKeepVal) {
-                    v_out = val[j][c];
-                } else {
-                    const uint32_t k = key[j][c];
-                    const uint32_t zbit = (negz[(4 * j + c) >> 5] >> ((4 * j + c) & 31)) & 1u;
-                    v_out = __uint_as_float((k & 0x80000000u) ? ((k & 0x7fffffffu) | (zbit << 31)) : ~k);
-                }
-                if (stage) {
-                    s_tok[pos] = t + c;
-                    s_w[pos] = v_out;
-                } else {
-                    idx[(int64_t)e * C + pos] = t + c;
-                    if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
-                    wt[(int64_t)e * C + pos] = v_out;
-                }
+            for (int c = 0; c < 4; ++c) {
+                eq[c] = key[j][c] == v;
+                gt[c] = key[j][c] > v;
+                ne += eq[c] ? 1 : 0;
+                ng += gt[c] ? 1 : 0;
             }
-            eqr += eq[c] ? 1 : 0;
-            gtr += gt[c] ? 1 : 0;
-        }
-        if (sm) {
-            if (vec_sm && t < T) {
-                *reinterpret_cast<int4*>(sm + t) = make_int4(slot[0], slot[1], slot[2], slot[3]);
-            } else {
+            int tot_eq, tot_gt;
+            int eqr = eqb + lanes_below(ne, tot_eq);
+            int gtr = gtb + lanes_below(ng, tot_gt);
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (t + c < T) sm[t + c] = slot[c];
+            for (int c = 0; c < 4; ++c) {
+                const bool sel = gt[c] || (eq[c] && eqr < need_eq);
+                const int pos = gtr + (eqr < need_eq ? eqr : need_eq);
+                if constexpr (kMode == 1) {
+                    // branch-free: every lane writes, a lane that selects nothing into its own unused slot
+                    const int dst = (sel && pos < C) ? pos : kSelStageC + lane;
+                    float v_out;
+                    if constexpr (kKeepVal) {
+                        v_out = val[j][c];
+                    } else {
+                        const uint32_t k = key[j][c];
+                        const uint32_t zbit = (negz[(4 * j + c) >> 5] >> ((4 * j + c) & 31)) & 1u;
+                        v_out = __uint_as_float((k & 0x80000000u) ? ((k & 0x7fffffffu) | (zbit << 31)) : ~k);
+                    }
+                    s_tok[dst] = t + c;
+                    s_w[dst] = v_out;
+                } else if (sel && pos < C) {
+                    float v_out;
+                    if constexpr (kKeepVal) {
+                        v_out = val[j][c];
+                    } else {
+                        const uint32_t k = key[j][c];
+                        const uint32_t zbit = (negz[(4 * j + c) >> 5] >> ((4 * j + c) & 31)) & 1u;
+                        v_out = __uint_as_float((k & 0x80000000u) ? ((k & 0x7fffffffu) | (zbit << 31)) : ~k);
+                    }
+                    if (kMode == 2 && stage) {
+                        s_tok[pos] = t + c;
+                        s_w[pos] = v_out;
+                    } else {
+                        idx[(int64_t)e * C + pos] = t + c;
+                        if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
+                        if (sm) sm[t + c] = pos;
+                        wt[(int64_t)e * C + pos] = v_out;
+                    }
+                }
+                eqr += eq[c] ? 1 : 0;
+                gtr += gt[c] ? 1 : 0;
             }
+            eqb += tot_eq;
+            gtb += tot_gt;
         }
-        eqb += tot_eq;
-        gtb += tot_gt;
+    };
+    if constexpr (KR <= 8) {
+        if (stage)
+            rounds(std::integral_constant<int, 1>{});
+        else
+            rounds(std::integral_constant<int, 0>{});
+    } else {
+        rounds(std::integral_constant<int, 2>{});
     }
     if (stage) {
         __syncthreads();
@@ -547,6 +569,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
             idx[(int64_t)e * C + i] = tt;
             wt[(int64_t)e * C + i] = s_w[i];
             if (tokmask) atomicOr(tokmask + (int64_t)tt * nw + (e >> 6), 1ull << (e & 63));
+            if (sm) sm[tt] = i;
         }
     }
 }
