@@ -301,7 +301,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
     __shared__ uint32_t s_bcast[3];
     __shared__ int s_cnt[2 * kSelV];
     __shared__ uint32_t s_cand[kSelFew];
-    __shared__ uint32_t s_ncand;
+    __shared__ uint32_t s_ncand;  // zeroed by every pass's scan; the early finish only follows a pass
     // staged tokens at hist[slot], weights at hist[1024 + slot]; slots kSelStageC + lane take the writes of
     // lanes that select nothing
     static_assert(kSelStageC + 64 <= kSelBins / 2, "staged selection fits the bins");
@@ -381,7 +381,12 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
             for (int j = 0; j < KR; ++j)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    if ((key[j][c] & mask) == prefix) s_cand[atomicAdd(&s_ncand, 1u)] = key[j][c];
+                    if ((key[j][c] & mask) == prefix) {
+                        // n_left keys pass this test (the bin count the scan reported), so a slot past the
+                        // array cannot occur; the bound keeps the LDS write local to s_cand regardless
+                        const uint32_t at = atomicAdd(&s_ncand, 1u);
+                        if (at < (uint32_t)kSelFew) s_cand[at] = key[j][c];
+                    }
             __syncthreads();
             if (w == 0) {
                 const int n = (int)n_left;
