@@ -321,7 +321,7 @@ convrot_status moe_gateup_swiglu(const int8_t* qx, const float* sx, int T, const
 convrot_status moe_down_proj(const int8_t* qa, const float* sa, int C, const convrot_moe_weights* w,
                              uint16_t* z_out, hipStream_t stream);
 
-/* Bytes of workspace moe_combine needs (slot map [E, T] int32 and token masks [T, ceil(E / 64)] uint64). */
+/* Bytes of workspace moe_combine needs (the slot table [T, E] int32: each token's position in each list). */
 size_t moe_combine_workspace_bytes(int T, int E);
 
 /* Combine stage: out[T, d] from z (device) [E*C, d] bf16, idx (device) [E, C] (each row strictly

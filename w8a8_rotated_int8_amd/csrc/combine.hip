@@ -6,9 +6,9 @@
 // element is summed by one lane, no atomics, so the sum order is fixed.
 //
 // A token's row is split over wavefronts of 64 chunks of 16 bytes (more, shorter wavefronts measured faster
-// than one per token).  In each, the token's mask word says which experts took it; lane e reads the slot map
-// entry of expert e only if its bit is set (up to 64 experts per word: about two loads per token instead of
-// 64 cache lines), a ballot gives the taking experts, and their rows are summed from the lowest expert up.
+// than one per token).  In each, lane e reads the slot-table entry of expert e (the token's entries for 64
+// experts are contiguous: one coalesced load), a ballot gives the taking experts, and their rows are summed
+// from the lowest expert up.  Two dependent loads per expert row (slot, then row and weight).
 // The row loads of up to kBatch experts are all issued before any of them is summed, so a token costs one
 // memory latency per kBatch experts rather than one per expert.  Lane l owns the chunks l, l + 64, ... of its wavefront's
 // part of the row.
@@ -22,8 +22,7 @@ constexpr int kBatch = 4;
 constexpr int kMaxChunks = 1;  // 16-byte chunks per lane: a d = 2048 row is split over 4 wavefronts
 
 template <int CH>  // 16-byte chunks (8 bf16) per lane
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ z, const int32_t* __restrict__ slotmap,
-                                                      const uint64_t* __restrict__ tokmask,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ z, const int32_t* __restrict__ slots,
                                                       const float* __restrict__ wt, int T, int E, int C, int d,
                                                       int split, uint16_t* __restrict__ out) {
     const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -39,11 +38,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[j][q] = 0.0f;
 
-    const int nw = (E + 63) >> 6;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        const uint64_t word = tokmask[(int64_t)t * nw + (e0 >> 6)];  // uniform over the wavefront
-        const int c = (e < E && ((word >> lane) & 1ull)) ? slotmap[(int64_t)e * T + t] : -1;
+        const int c = e < E ? slots[(int64_t)t * E + e] : -1;
         const float w = (c >= 0) ? wt[(int64_t)e * C + c] : 0.0f;
         uint64_t taken = __ballot(c >= 0);
         while (taken) {
@@ -103,17 +100,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const uint64_t* tokmask, const float* wt, int T,
-                          int E, int C, int d, uint16_t* out, hipStream_t st) {
+hipError_t launch_combine(const uint16_t* z, const int32_t* slots, const float* wt, int T, int E, int C, int d,
+                          uint16_t* out, hipStream_t st) {
     if (T == 0) return hipSuccess;
     // chunks per lane with one wavefront per token, then split over wavefronts to at most kMaxChunks each
     const int ch_one = (d / 8 + 63) / 64;
     const int split = (ch_one + kMaxChunks - 1) / kMaxChunks;
     const int ch = (ch_one + split - 1) / split;
     const dim3 grid((unsigned)(((int64_t)T * split + 3) / 4)), block(256);
-    if (ch <= 1) combine_kernel<1><<<grid, block, 0, st>>>(z, slotmap, tokmask, wt, T, E, C, d, split, out);
-    else if (ch <= 2) combine_kernel<2><<<grid, block, 0, st>>>(z, slotmap, tokmask, wt, T, E, C, d, split, out);
-    else if (ch <= 4) combine_kernel<4><<<grid, block, 0, st>>>(z, slotmap, tokmask, wt, T, E, C, d, split, out);
+    if (ch <= 1) combine_kernel<1><<<grid, block, 0, st>>>(z, slots, wt, T, E, C, d, split, out);
+    else if (ch <= 2) combine_kernel<2><<<grid, block, 0, st>>>(z, slots, wt, T, E, C, d, split, out);
+    else if (ch <= 4) combine_kernel<4><<<grid, block, 0, st>>>(z, slots, wt, T, E, C, d, split, out);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -42,8 +42,7 @@ struct Carver {
 
 struct MoeBuffers {
     float* probs_t;
-    int32_t* slotmap;
-    uint64_t* tokmask;
+    int32_t* slots;  // [T, E]: position of token t in expert e's list, or -1
     int8_t* qx;
     float* sx;
     int32_t* idx;
@@ -60,8 +59,7 @@ size_t plan_moe(void* ws, int T, int C, const convrot_moe_weights& w, MoeBuffers
     const size_t S = (size_t)w.E * (size_t)C;
     MoeBuffers m;
     m.probs_t = cv.take<float>((size_t)w.E * T);
-    m.slotmap = cv.take<int32_t>((size_t)w.E * T);
-    m.tokmask = cv.take<uint64_t>((size_t)T * ((w.E + 63) / 64));
+    m.slots = cv.take<int32_t>((size_t)T * w.E);
     m.qx = cv.take<int8_t>((size_t)T * w.d);
     m.sx = cv.take<float>((size_t)T);
     m.idx = cv.take<int32_t>(S);
@@ -177,14 +175,14 @@ convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_log
     const int64_t t1 = (int64_t)T * kRotqBesideSoftmaxPct / 100;
     const bool split = w.E <= 64 && crk::select_rotq_supported(T, w.E, w.d, w.group_gu);
     if (split) {
-        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, b.tokmask, x, w.d, w.group_gu, b.qx, b.sx,
+        CRK_TRY(crk::launch_softmax_rotq(router_logits, T, w.E, b.probs_t, b.slots, x, w.d, w.group_gu, b.qx, b.sx,
                                          t1, stream));
-        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, x, w.d, w.group_gu, b.qx,
+        CRK_TRY(crk::launch_select_rotq(b.probs_t, T, w.E, C, idx, wt, b.slots, x, w.d, w.group_gu, b.qx,
                                         b.sx, t1, b.esync, stream));
     } else {
-        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, b.tokmask, stream));
+        CRK_TRY(crk::launch_softmax_t(router_logits, 0, T, w.E, b.probs_t, nullptr, b.slots, stream));
         CRK_TRY(crk::launch_rotq_act(x, T, w.d, w.group_gu, b.qx, b.sx, nullptr, stream));
-        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slotmap, b.tokmask, b.esync, stream));
+        CRK_TRY(crk::launch_select_topc(b.probs_t, T, w.E, C, idx, wt, b.slots, b.esync, stream));
     }
     const crk::GemmProblem gu = gateup_problem(b.qx, b.sx, T, idx, C, w, b.a);
     const crk::GemmProblem dn = down_problem(b.qa, b.sa, C, w, b.z);
@@ -195,7 +193,7 @@ convrot_status enqueue_forward(const uint16_t* x, int T, const float* router_log
         CRK_TRY(crk::launch_rotq_act(b.a, S, w.I, w.group_dn, b.qa, b.sa, nullptr, stream));
         CRK_TRY(crk::launch_grouped_gemm(dn, stream));
     }
-    CRK_TRY(crk::launch_combine(b.z, b.slotmap, b.tokmask, wt, T, w.E, C, w.d, out, stream));
+    CRK_TRY(crk::launch_combine(b.z, b.slots, wt, T, w.E, C, w.d, out, stream));
     return CONVROT_OK;
 }
 
@@ -504,7 +502,7 @@ convrot_status moe_route_expert_choice(const float* in, int is_probs, int T, int
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
     float* probs_t = static_cast<float*>(ws);
     CRK_TRY(crk::launch_softmax_t(in, is_probs ? 1 : 0, T, E, probs_t, probs_out, nullptr, stream));
-    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, nullptr, nullptr, stream));
+    CRK_TRY(crk::launch_select_topc(probs_t, T, E, C, idx_out, wt_out, nullptr, nullptr, stream));
     return CONVROT_OK;
 }
 
@@ -532,8 +530,7 @@ convrot_status moe_down_proj(const int8_t* qa, const float* sa, int C, const con
 size_t moe_combine_workspace_bytes(int T, int E) {
     if (T < 1 || E < 1) return 0;
     Carver cv(nullptr);
-    cv.take<int32_t>((size_t)E * T);
-    cv.take<uint64_t>((size_t)T * ((E + 63) / 64));
+    cv.take<int32_t>((size_t)T * E);
     return cv.used;
 }
 
@@ -547,10 +544,9 @@ convrot_status moe_combine(const uint16_t* z, const int32_t* idx, const float* w
     if (!ws || ws_bytes < moe_combine_workspace_bytes(T, E)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(ws)) return CONVROT_ERR_ALIGN;
     Carver cv(ws);
-    int32_t* slotmap = cv.take<int32_t>((size_t)E * T);
-    uint64_t* tokmask = cv.take<uint64_t>((size_t)T * ((E + 63) / 64));
-    CRK_TRY(crk::launch_build_slotmap(idx, T, E, C, slotmap, tokmask, stream));
-    CRK_TRY(crk::launch_combine(z, slotmap, tokmask, wt, T, E, C, d, out, stream));
+    int32_t* slots = cv.take<int32_t>((size_t)T * E);
+    CRK_TRY(crk::launch_build_slots(idx, T, E, C, slots, stream));
+    CRK_TRY(crk::launch_combine(z, slots, wt, T, E, C, d, out, stream));
     return CONVROT_OK;
 }
 

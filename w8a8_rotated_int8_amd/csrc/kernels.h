@@ -29,29 +29,29 @@ hipError_t launch_quantize_prerotated(const float* r, int64_t rows, int K, int b
 
 // ---- routing ------------------------------------------------------------------------------------------
 // probs^T [E, T] from logits [T, E] (or a transpose of given probabilities); optional probs [T, E] copy.
-// tokmask [T, ceil(E / 64)] (or nullptr): cleared for the selection that follows.
+// slots [T, E] (or nullptr): the slot table (slots[t, e] = position of token t in expert e's list, or -1), its
+// rows filled with -1 for the selection that follows.
 hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* probs_t, float* probs_out,
-                            uint64_t* tokmask, hipStream_t st);
-// Per expert: top-C selection on probs_t[e, :]; writes idx [E, C], wt [E, C] and, if slotmap != nullptr,
-// slotmap [E, T] (position of token t in expert e's list, or -1); if tokmask != nullptr, sets bit e of token t's
-// mask words for every selected token (the words must have been cleared).
+                            int32_t* slots, hipStream_t st);
 // Router softmax (E <= 64, logits) and token rotate+quantise (fast shapes) in one launch; returns
 // hipErrorNotSupported, having launched nothing, for other shapes.
 // softmax of all T tokens and rotate+quantise of token rows [0, rows) in one launch
-hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, uint64_t* tokmask,
+hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, int32_t* slots,
                                const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t rows,
                                hipStream_t st);
+// Per expert: top-C selection on probs_t[e, :]; writes idx [E, C], wt [E, C] and, if slots != nullptr, the
+// slot-table entries of the tokens it takes (the table must hold -1 elsewhere, as the softmax leaves it).
 // selection of all E experts and rotate+quantise of token rows [row0, T) in one launch
 bool select_rotq_supported(int T, int E, int K, int group);
-hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
-                              uint64_t* tokmask, const uint16_t* x, int K, int group, int8_t* qx, float* sx,
-                              int64_t row0, uint32_t* esync, hipStream_t st);
+hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slots,
+                              const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t row0,
+                              uint32_t* esync, hipStream_t st);
 // esync (nullable): the 2E counters of launch_moe_experts, zeroed by the selection of each expert.
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
-                              int32_t* slotmap, uint64_t* tokmask, uint32_t* esync, hipStream_t st);
-// slotmap [E, T] and the token masks [T, ceil(E / 64)] from idx [E, C].
-hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, uint64_t* tokmask,
-                                hipStream_t st);
+                              int32_t* slots, uint32_t* esync, hipStream_t st);
+// The slot table [T, E] of the lists idx [E, C] (-1 where a token is in no list; entries outside [0, T)
+// ignored).
+hipError_t launch_build_slots(const int32_t* idx, int T, int E, int C, int32_t* slots, hipStream_t st);
 
 // ---- grouped INT8 GEMM --------------------------------------------------------------------------------
 enum class Epi : int { kI32 = 0, kBf16 = 1, kSwiGLU = 2 };
@@ -89,7 +89,7 @@ hipError_t launch_moe_experts(const GemmProblem& gu, const GemmProblem& dn, cons
 bool moe_experts_supported(const GemmProblem& gu, const GemmProblem& dn, int group);
 
 // ---- combine ------------------------------------------------------------------------------------------
-hipError_t launch_combine(const uint16_t* z, const int32_t* slotmap, const uint64_t* tokmask, const float* wt, int T,
-                          int E, int C, int d, uint16_t* out, hipStream_t st);
+hipError_t launch_combine(const uint16_t* z, const int32_t* slots, const float* wt, int T, int E, int C, int d,
+                          uint16_t* out, hipStream_t st);
 
 }  // namespace crk

@@ -12,12 +12,10 @@
 //                passes.  Then one ordered compaction keeps every token above the threshold and the
 //                lowest-index tokens equal to it.  The list comes out in ascending token order without a sort;
 //                ties go to the lower token index by construction.
-//  Slot map: slotmap[e, t] = position of t in expert e's list.  The selections write only the entries of the
-//                tokens they take, at the same time as the token mask bit; the combine reads an entry only
-//                where that bit is set (build_slotmap, for the stand-alone combine, writes -1 everywhere else).
-//  Token masks: where asked for, bit e % 64 of word t * ceil(E / 64) + e / 64 is set when expert e takes token
-//  t (OR is order-independent, so the mask does not depend on which workgroup sets its bit first).  The softmax
-//  launch, which runs before the selection, clears the words of its tokens.
+//  Slot table: slots[t, e] = position of token t in expert e's list, or -1, token-major so that one
+//                coalesced load gives a token's entries for 64 experts.  The softmax launch, which runs before
+//                the selection, fills the rows of its tokens with -1; the selections then write the entries of
+//                the tokens they take.  build_slots does both for a given list (the stand-alone combine).
 #include <type_traits>
 
 #include "device_common.h"
@@ -53,7 +51,7 @@ struct SoftmaxLds {
 template <int EF>
 __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int is_probs, int T, int E_arg,
                                              float* __restrict__ probs_t, float* __restrict__ probs_out,
-                                             uint64_t* __restrict__ tokmask, int b, SoftmaxLds& lds) {
+                                             int32_t* __restrict__ slots, int b, SoftmaxLds& lds) {
     const int E = EF > 0 ? EF : E_arg;
     float* const tile = lds.tile;
     float* const tr = lds.tr;
@@ -61,7 +59,16 @@ __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int i
     const int t0 = b * kSmTok;
     const int ntok = (T - t0) < kSmTok ? (T - t0) : kSmTok;
     const int tid = threadIdx.x, tok = tid >> 3, eg = tid & 7;
-    if (tokmask && tid < ntok) tokmask[t0 + tid] = 0ull;  // E <= 64: one mask word per token
+    if (slots) {  // the tile's rows of the slot table (contiguous) to -1
+        int32_t* const srow = slots + (int64_t)t0 * E;
+        const int ns = ntok * E;
+        if (EF == 64 && ntok == kSmTok && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) reinterpret_cast<int4*>(srow)[tid + 256 * k] = make_int4(-1, -1, -1, -1);
+        } else {
+            for (int i = tid; i < ns; i += 256) srow[i] = -1;
+        }
+    }
     const float* src = in + (int64_t)t0 * E;
     const int n = ntok * E;  // the tile is contiguous in global memory
     if (E == 64 && ntok == kSmTok && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
@@ -153,12 +160,12 @@ __device__ __forceinline__ void softmax_tile(const float* __restrict__ in, int i
 
 __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __restrict__ in, int is_probs, int T, int E,
                                                               float* __restrict__ probs_t, float* __restrict__ probs_out,
-                                                              uint64_t* __restrict__ tokmask) {
+                                                              int32_t* __restrict__ slots) {
     __shared__ SoftmaxLds lds;
     if (E == 64)
-        softmax_tile<64>(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x, lds);
+        softmax_tile<64>(in, is_probs, T, E, probs_t, probs_out, slots, blockIdx.x, lds);
     else
-        softmax_tile<0>(in, is_probs, T, E, probs_t, probs_out, tokmask, blockIdx.x, lds);
+        softmax_tile<0>(in, is_probs, T, E, probs_t, probs_out, slots, blockIdx.x, lds);
 }
 
 // The router softmax and token rotate+quantise in one launch: they do not depend on each other, so the first
@@ -166,16 +173,16 @@ __global__ __launch_bounds__(256) void softmax_t_small_kernel(const float* __res
 // rotate+quantise workgroups fill the CUs the short softmax leaves idle, with no second stream to join.
 template <int G, int R>
 __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restrict__ logits, int T, int E,
-                                                           float* __restrict__ probs_t, uint64_t* __restrict__ tokmask,
+                                                           float* __restrict__ probs_t, int32_t* __restrict__ slots,
                                                            int nsm, const uint16_t* __restrict__ x, int K,
                                                            int8_t* __restrict__ qx, float* __restrict__ sx,
                                                            int64_t rows) {
     __shared__ SoftmaxLds lds;
     if ((int)blockIdx.x < nsm) {  // workgroup-uniform
         if (E == 64)
-            softmax_tile<64>(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x, lds);
+            softmax_tile<64>(logits, 0, T, E, probs_t, nullptr, slots, blockIdx.x, lds);
         else
-            softmax_tile<0>(logits, 0, T, E, probs_t, nullptr, tokmask, blockIdx.x, lds);
+            softmax_tile<0>(logits, 0, T, E, probs_t, nullptr, slots, blockIdx.x, lds);
         return;
     }
     const int64_t row = (int64_t)(blockIdx.x - nsm) * 4 + (threadIdx.x >> 6);
@@ -186,13 +193,11 @@ __global__ __launch_bounds__(256) void softmax_rotq_kernel(const float* __restri
 // ---- softmax, any E (one thread per token) ------------------------------------------------------------
 __global__ __launch_bounds__(256) void softmax_t_kernel(const float* __restrict__ in, int is_probs, int T, int E,
                                                         float* __restrict__ probs_t, float* __restrict__ probs_out,
-                                                        uint64_t* __restrict__ tokmask) {
+                                                        int32_t* __restrict__ slots) {
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= T) return;
-    if (tokmask) {
-        const int nw = (E + 63) >> 6;
-        for (int i = 0; i < nw; ++i) tokmask[(int64_t)t * nw + i] = 0ull;
-    }
+    if (slots)
+        for (int e = 0; e < E; ++e) slots[(int64_t)t * E + e] = -1;
     const float* l = in + (int64_t)t * E;
     if (is_probs) {
         for (int e = 0; e < E; ++e) {
@@ -294,8 +299,8 @@ __device__ __forceinline__ int lanes_below(int v, int& total) {
 template <int KR>
 __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ probs_t, int T, int C,
                                                     int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                    int32_t* __restrict__ slotmap, uint64_t* __restrict__ tokmask,
-                                                    int nw, int e, uint32_t* __restrict__ esync) {
+                                                    int32_t* __restrict__ slots, int E, int e,
+                                                    uint32_t* __restrict__ esync) {
     __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
     __shared__ uint32_t s_red[2 * kSelV];
     __shared__ uint32_t s_bcast[3];
@@ -490,7 +495,6 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
         eqb += x < w ? s_cnt[x] : 0;
         gtb += x < w ? s_cnt[kSelV + x] : 0;
     }
-    int32_t* sm = slotmap ? slotmap + (int64_t)e * T : nullptr;
     // C <= kSelStageC: the selected tokens and weights go to LDS by slot (the bins are free: the last read of
     // them was before the last barrier), and leave in slot order once all are placed.  Up to 8 rounds the rounds
     // are compiled once per choice (workgroup-uniform), so neither path carries the other's branches; more
@@ -547,8 +551,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
                         s_w[pos] = v_out;
                     } else {
                         idx[(int64_t)e * C + pos] = t + c;
-                        if (tokmask) atomicOr(tokmask + (int64_t)(t + c) * nw + (e >> 6), 1ull << (e & 63));
-                        if (sm) sm[t + c] = pos;
+                        if (slots) slots[(int64_t)(t + c) * E + e] = pos;
                         wt[(int64_t)e * C + pos] = v_out;
                     }
                 }
@@ -573,8 +576,7 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
             const int tt = s_tok[i];
             idx[(int64_t)e * C + i] = tt;
             wt[(int64_t)e * C + i] = s_w[i];
-            if (tokmask) atomicOr(tokmask + (int64_t)tt * nw + (e >> 6), 1ull << (e & 63));
-            if (sm) sm[tt] = i;
+            if (slots) slots[(int64_t)tt * E + e] = i;
         }
     }
 }
@@ -582,10 +584,9 @@ __device__ __forceinline__ void select_topc_v_block(const float* __restrict__ pr
 template <int KR>
 __global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                    int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                   int32_t* __restrict__ slotmap,
-                                                                   uint64_t* __restrict__ tokmask, int nw,
+                                                                   int32_t* __restrict__ slots, int E,
                                                                    uint32_t* __restrict__ esync) {
-    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x, esync);
+    select_topc_v_block<KR>(probs_t, T, C, idx, wt, slots, E, blockIdx.x, esync);
 }
 
 // The selection and the rest of the token rotate+quantise in one launch: the first E workgroups select (one
@@ -593,13 +594,12 @@ __global__ __launch_bounds__(kSelV * 64) void select_topc_v_kernel(const float* 
 template <int KR, int G, int R>
 __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __restrict__ probs_t, int T, int C, int E,
                                                                  int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                 int32_t* __restrict__ slotmap,
-                                                                 uint64_t* __restrict__ tokmask, int nw,
+                                                                 int32_t* __restrict__ slots,
                                                                  const uint16_t* __restrict__ x, int K,
                                                                  int8_t* __restrict__ qx, float* __restrict__ sx,
                                                                  int64_t row0, uint32_t* __restrict__ esync) {
     if ((int)blockIdx.x < E) {  // workgroup-uniform
-        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, blockIdx.x, esync);
+        select_topc_v_block<KR>(probs_t, T, C, idx, wt, slots, E, blockIdx.x, esync);
         return;
     }
     const int64_t row = row0 + (int64_t)(blockIdx.x - E) * kSelV + (threadIdx.x >> 6);
@@ -610,8 +610,7 @@ __global__ __launch_bounds__(kSelV * 64) void select_rotq_kernel(const float* __
 // Any T: keys re-read from global memory in each pass.
 __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* __restrict__ probs_t, int T, int C,
                                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                                  int32_t* __restrict__ slotmap,
-                                                                  uint64_t* __restrict__ tokmask, int nw,
+                                                                  int32_t* __restrict__ slots, int E,
                                                                   uint32_t* __restrict__ esync) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_prefix, s_remaining;
@@ -689,49 +688,42 @@ __global__ __launch_bounds__(kSelThreads) void select_topc_kernel(const float* _
         if (sel && pos < C) {
             idx[(int64_t)e * C + pos] = t;
             wt[(int64_t)e * C + pos] = pv;
-            if (tokmask) atomicOr(tokmask + (int64_t)t * nw + (e >> 6), 1ull << (e & 63));
+            if (slots) slots[(int64_t)t * E + e] = pos;
         }
-        if (valid && slotmap) slotmap[(int64_t)e * T + t] = sel ? pos : -1;
         carry_eq += tot_eq;
         carry_sel += tot_sel;
     }
 }
 
-__global__ __launch_bounds__(1024) void build_slotmap_kernel(const int32_t* __restrict__ idx, int T, int C,
-                                                             int32_t* __restrict__ slotmap,
-                                                             uint64_t* __restrict__ tokmask, int nw) {
-    const int e = blockIdx.x;
-    int32_t* row = slotmap + (int64_t)e * T;
-    for (int t = threadIdx.x; t < T; t += 1024) row[t] = -1;
-    __syncthreads();
-    for (int c = threadIdx.x; c < C; c += 1024) {
-        const int t = idx[(int64_t)e * C + c];
-        if (t >= 0 && t < T) {  // entries outside [0, T) are ignored
-            row[t] = c;
-            atomicOr(tokmask + (int64_t)t * nw + (e >> 6), 1ull << (e & 63));
-        }
-    }
+// Entries of the given lists (idx [E, C]); tokens outside [0, T) are ignored.  The table is -1 beforehand.
+__global__ __launch_bounds__(256) void build_slots_kernel(const int32_t* __restrict__ idx, int T, int E, int C,
+                                                          int32_t* __restrict__ slots) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)E * C) return;
+    const int e = (int)(i / C), c = (int)(i - (int64_t)e * C);
+    const int t = idx[i];
+    if (t >= 0 && t < T) slots[(int64_t)t * E + e] = c;
 }
 
-__global__ __launch_bounds__(256) void clear_words_kernel(uint64_t* __restrict__ p, int64_t n) {
+__global__ __launch_bounds__(256) void fill_minus_one_kernel(int32_t* __restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0ull;
+    if (i < n) p[i] = -1;
 }
 
 }  // namespace
 
 hipError_t launch_softmax_t(const float* in, int is_probs, int T, int E, float* probs_t, float* probs_out,
-                            uint64_t* tokmask, hipStream_t st) {
+                            int32_t* slots, hipStream_t st) {
     if (E <= 64)
         softmax_t_small_kernel<<<dim3((T + kSmTok - 1) / kSmTok), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t,
-                                                                                      probs_out, tokmask);
+                                                                                      probs_out, slots);
     else
         softmax_t_kernel<<<dim3((T + 255) / 256), dim3(256), 0, st>>>(in, is_probs, T, E, probs_t, probs_out,
-                                                                      tokmask);
+                                                                      slots);
     return hipGetLastError();
 }
 
-hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, uint64_t* tokmask,
+hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t, int32_t* slots,
                                const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t rows,
                                hipStream_t st) {
     if (T <= 0) return hipSuccess;
@@ -742,7 +734,7 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
     const int R = K / (8 * group);
 #define CRK_SR(GG, RR)                                                                                  \
     if (group == GG && R == RR) {                                                                       \
-        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, tokmask, nsm, x, K, qx, sx, \
+        softmax_rotq_kernel<GG, RR><<<grid, block, 0, st>>>(logits, T, E, probs_t, slots, nsm, x, K, qx, sx,   \
                                                             rows);                                            \
         return hipGetLastError();                                                                       \
     }
@@ -757,12 +749,10 @@ hipError_t launch_softmax_rotq(const float* logits, int T, int E, float* probs_t
 }
 
 hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt,
-                              int32_t* slotmap, uint64_t* tokmask, uint32_t* esync, hipStream_t st) {
-    const int nw = (E + 63) >> 6;
+                              int32_t* slots, uint32_t* esync, hipStream_t st) {
 #define CRK_SEL(K)                                                                                              \
     if (T <= kSelV * 256 * K) {                                                                                 \
-        select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, \
-                                                                      nw, esync);                               \
+        select_topc_v_kernel<K><<<dim3(E), dim3(kSelV * 64), 0, st>>>(probs_t, T, C, idx, wt, slots, E, esync); \
         return hipGetLastError();                                                                               \
     }
     CRK_SEL(1)
@@ -771,7 +761,7 @@ hipError_t launch_select_topc(const float* probs_t, int T, int E, int C, int32_t
     CRK_SEL(8)
     CRK_SEL(16)
 #undef CRK_SEL
-    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slotmap, tokmask, nw, esync);
+    select_topc_kernel<<<dim3(E), dim3(kSelThreads), 0, st>>>(probs_t, T, C, idx, wt, slots, E, esync);
     return hipGetLastError();
 }
 
@@ -780,18 +770,17 @@ bool select_rotq_supported(int T, int E, int K, int group) {
     return T >= 1 && T <= kSelV * 256 * 8 && E >= 1 && (group == 256 || group == 64) && (R == 1 || R == 2 || R == 4);
 }
 
-hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slotmap,
-                              uint64_t* tokmask, const uint16_t* x, int K, int group, int8_t* qx, float* sx,
-                              int64_t row0, uint32_t* esync, hipStream_t st) {
-    const int nw = (E + 63) >> 6;
+hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t* idx, float* wt, int32_t* slots,
+                              const uint16_t* x, int K, int group, int8_t* qx, float* sx, int64_t row0,
+                              uint32_t* esync, hipStream_t st) {
     if (!select_rotq_supported(T, E, K, group) || row0 < 0 || row0 > T) return hipErrorNotSupported;
     const int R = K / (8 * group);
     const int64_t nrot = (T - row0 + kSelV - 1) / kSelV;
     const dim3 grid((unsigned)(E + nrot)), block(kSelV * 64);
 #define CRK_SR2(KK, GG, RR)                                                                                 \
     if (T <= kSelV * 256 * KK && group == GG && R == RR) {                                                  \
-        select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slotmap, tokmask, nw, \
-                                                               x, K, qx, sx, row0, esync);                 \
+        select_rotq_kernel<KK, GG, RR><<<grid, block, 0, st>>>(probs_t, T, C, E, idx, wt, slots, x, K, qx, sx, \
+                                                               row0, esync);                               \
         return hipGetLastError();                                                                           \
     }
 #define CRK_SR2_G(KK) CRK_SR2(KK, 256, 1) CRK_SR2(KK, 256, 2) CRK_SR2(KK, 256, 4) CRK_SR2(KK, 64, 1) \
@@ -805,12 +794,10 @@ hipError_t launch_select_rotq(const float* probs_t, int T, int E, int C, int32_t
     return hipErrorNotSupported;
 }
 
-hipError_t launch_build_slotmap(const int32_t* idx, int T, int E, int C, int32_t* slotmap, uint64_t* tokmask,
-                                hipStream_t st) {
-    const int nw = (E + 63) >> 6;
-    const int64_t words = (int64_t)T * nw;
-    clear_words_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(tokmask, words);
-    build_slotmap_kernel<<<dim3(E), dim3(1024), 0, st>>>(idx, T, C, slotmap, tokmask, nw);
+hipError_t launch_build_slots(const int32_t* idx, int T, int E, int C, int32_t* slots, hipStream_t st) {
+    const int64_t n = (int64_t)T * E, m = (int64_t)E * C;
+    fill_minus_one_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(slots, n);
+    build_slots_kernel<<<dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st>>>(idx, T, E, C, slots);
     return hipGetLastError();
 }
 
