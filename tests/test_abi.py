@@ -99,7 +99,7 @@ def test_moe_forward_validation(L):
     f = L.moe_expert_choice_forward
     w = _weights()
     need = L.moe_expert_choice_workspace_bytes(8192, 256, ctypes.byref(w))
-    # probs^T + slot map (E*T*4 each), qx + sx, idx + wt, a (bf16) + qa + sa, z (bf16)
+    # probs^T + slot table (E*T*4 each), qx + sx, idx + wt, a (bf16) + qa + sa, z (bf16)
     S = 64 * 256
     assert need >= 2 * 64 * 8192 * 4 + 8192 * 2048 + 8192 * 4 + 2 * S * 4 + S * 1536 * 3 + S * 4 + S * 2048 * 2
     args = lambda T=8192, C=256, ww=w, ws=P, nb=need: (P, T, P, C, ctypes.byref(ww), P, None, None, ws, nb, None)
