@@ -347,6 +347,10 @@ SMALL = [
     synth.MoEShape(T=500, d=4096, E=2, I=64, C=10, g_gu=256, g_dn=64),
     # more than 64 experts: softmax, rotate+quantise and selection as separate launches
     synth.MoEShape(T=200, d=256, E=80, I=64, C=5, g_gu=64, g_dn=64),
+    # one expert taking every token (all probabilities 1: ties throughout, one slot-table column)
+    synth.MoEShape(T=50, d=512, E=1, I=64, C=50, g_gu=64, g_dn=64),
+    # 64 experts (the softmax tile compiled for E = 64) with a ragged last tile of 4 tokens
+    synth.MoEShape(T=100, d=512, E=64, I=64, C=10, g_gu=64, g_dn=64),
 ]
 
 
